@@ -1,0 +1,219 @@
+"""Throughput of the fused varlen / GQA attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--cpu-heads N]
+
+One step = one call of the forward entry point over the whole workload (the
+complete hot path: a single fused kernel launch), inputs already resident in
+HBM, outputs preallocated.  The default workload is the long-context packed
+batch: lengths [8192, 4096, 2048, 2048] (16384 tokens), H=64, Hkv=8, D=128,
+bf16, causal.
+
+Prints ONE JSON line.  FLOPs are algorithmic: 4*D per visible (query, key)
+pair per head, counted exactly from the sequence lengths and the mask.  Time
+comes from HIP events recorded on the stream the kernel runs on (torch's
+current stream), bracketed by device synchronisation.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "varlen causal GQA attn fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["variable_length_gqa_amd/csrc/attn_fwd.hip",
+                  "variable_length_gqa_amd/csrc/fwd_params.h"]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(workload)
+    if not rec or rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def make_step(name, dev):
+    import torch
+
+    import variable_length_gqa_amd as vg
+    from variable_length_gqa_amd import flops as F
+    from variable_length_gqa_amd import workloads as W
+
+    x = W.workload(name)
+    if isinstance(x, W.Varlen):
+        xd = x.to(dev)
+        out = torch.empty_like(xd.q)
+        lse = torch.empty((xd.q.shape[0], x.num_heads), dtype=torch.float32, device=dev)
+
+        def step():
+            vg.varlen_attention_fwd(xd.q, xd.k, xd.v, xd.cu_q, xd.cu_k, x.batch_size,
+                                    x.num_heads, x.num_kv_heads, x.max_seqlen_q, x.max_seqlen_k,
+                                    x.head_dim, x.causal, out=out, lse=lse)
+
+        flops = F.attention_flops(x.lengths_q, x.lengths_k, x.num_heads, x.head_dim, x.causal)
+        eb = x.q.element_size()
+        io = F.io_bytes(sum(x.lengths_q), sum(x.lengths_k), x.num_heads, x.num_kv_heads,
+                        x.head_dim, eb)
+        cfg = {"workload": name, "layout": "packed varlen", "lengths": x.lengths_q,
+               "total_tokens": sum(x.lengths_q), "heads": x.num_heads,
+               "kv_heads": x.num_kv_heads, "head_dim": x.head_dim, "causal": x.causal}
+        dt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[x.q.dtype]
+        return x, step, flops, io, cfg, dt
+    dd = x.to(dev)
+    B, H, Sq, D = x.q.shape
+    n = x.kv_seq_len if x.kv_seq_len is not None else x.k.shape[2]
+    flops = F.attention_flops([Sq] * B, [n] * B, H, D, x.causal, x.window)
+    if x.scales:
+        out = torch.empty(dd.q.shape, dtype=torch.uint8, device=dev)
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+        o_scale = _fp8_o_scale()
+        s = x.scales
+
+        def step():
+            vg.flash_attention_fwd_fp8(dd.q, dd.k, dd.v, H, x.num_kv_heads, D, x.causal,
+                                       s["q_scale"], s["k_scale"], s["v_scale"], o_scale,
+                                       out=out, lse=lse)
+        dt, eb = "fp8", 1
+    else:
+        out = torch.empty_like(dd.q)
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+
+        def step():
+            vg.flash_attention_fwd(dd.q, dd.k, dd.v, H, x.num_kv_heads, D, x.causal, x.window,
+                                   x.kv_seq_len, out=out, lse=lse)
+        dt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[x.q.dtype]
+        eb = x.q.element_size()
+    io = F.io_bytes(B * Sq, B * n, H, x.num_kv_heads, D, eb)
+    cfg = {"workload": name, "layout": "dense", "batch": B, "seqlen_q": Sq, "kv_seq_len": n,
+           "kv_capacity": x.k.shape[2], "heads": H, "kv_heads": x.num_kv_heads, "head_dim": D,
+           "causal": x.causal, "window": x.window}
+    return x, step, flops, io, cfg, dt
+
+
+def _fp8_o_scale():
+    with open(os.path.join(ROOT, "tests", "golden", "fp8_o_scale.json")) as f:
+        return json.load(f)["o_scale"]
+
+
+def cpu_baseline(name, x, n_heads, unit_scale):
+    """The f64 oracle, as it stands, on a bounded sample of the same workload:
+    the first ``n_heads`` query heads of every sequence, all worker processes."""
+    import oracle
+    from oracle.attention import default_workers
+    from variable_length_gqa_amd import flops as F
+    from variable_length_gqa_amd import workloads as W
+
+    workers = default_workers()
+    heads = list(range(n_heads))
+    t0 = time.perf_counter()
+    if isinstance(x, W.Varlen):
+        oracle.varlen_attention_fwd(x.q, x.k, x.v, x.cu_q, x.cu_k, x.num_heads, x.num_kv_heads,
+                                    x.causal, workers=workers, heads=heads)
+        fl = F.attention_flops(x.lengths_q, x.lengths_k, n_heads, x.head_dim, x.causal)
+    else:
+        B, H, Sq, D = x.q.shape
+        n = x.kv_seq_len if x.kv_seq_len is not None else x.k.shape[2]
+        if x.scales:
+            s = x.scales
+            oracle.flash_attention_fwd_fp8(x.q, x.k, x.v, H, x.num_kv_heads, x.causal,
+                                           s["q_scale"], s["k_scale"], s["v_scale"], 1.0,
+                                           workers=workers, heads=heads)
+        else:
+            oracle.flash_attention_fwd(x.q, x.k, x.v, H, x.num_kv_heads, x.causal, x.window,
+                                       x.kv_seq_len, workers=workers, heads=heads)
+        fl = F.attention_flops([Sq] * B, [n] * B, n_heads, D, x.causal, x.window)
+    secs = time.perf_counter() - t0
+    return {"value": fl / secs / unit_scale, "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"query heads 0..{n_heads - 1} of {x.num_heads} of every sequence "
+                      f"({fl:.3e} algorithmic FLOPs, {secs:.1f} s wall, f64 NumPy, "
+                      f"one process per core, masked scores computed too)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="varlen_bf16_long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward shards across GPUs by heads or by "
+              "sequences with no exchange, and this build runs and reports a single GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    x, step, flops, io, cfg, dt = make_step(args.workload, dev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dt]
+    traffic = measured_traffic(args.workload)
+
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shapes)",
+        "config": cfg,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
+        "flops_per_step": flops, "io_bytes_per_step": io,
+        "io_gbs": round(io / (ms * 1e-3) / 1e9, 1), "wall_s_timed": round(wall, 3),
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.workload, x, min(args.cpu_heads, x.num_heads),
+                                           1e12)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

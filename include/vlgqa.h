@@ -1,0 +1,143 @@
+/*
+ * vlgqa.h -- C ABI of the MI355X (gfx950) attention forward library.
+ *
+ * Three entry points: the packed variable-length forward, the dense forward
+ * with a KV-capacity stride and sliding window, and the FP8 dense forward.
+ * Each computes, for every query row i of every (sequence, query head h):
+ *
+ *     kv_head = h / (num_heads / num_kv_heads)              (GQA, no repeat)
+ *     s_j     = scale * <q_i, k_j>,   scale = 1/sqrt(head_dim)
+ *     O_i     = sum_{j visible} softmax(s)_j v_j,   LSE_i = ln sum_{j visible} exp(s_j)
+ *
+ * visible: causal -> j <= i + (Lk - Lq)  (queries are the newest Lq positions);
+ *          window W > 0 -> additionally j >= i + (Lk - Lq) - W + 1 (the W most
+ *          recent keys; a window implies the causal bound).
+ * A row that sees no key gets O = 0 and LSE = -inf.
+ *
+ * Conventions shared by all entry points
+ *   - Every tensor pointer is DEVICE memory owned by the caller; inputs are
+ *     only read.  out and lse are written for every valid row and nothing
+ *     else (rows of other sequences, padding and capacity tails are left
+ *     untouched).
+ *   - Tensors are contiguous in the layouts stated per entry point; extents
+ *     that a tensor's shape would carry are passed as scalars.
+ *   - The library allocates nothing, frees nothing and never synchronises:
+ *     kernels are enqueued on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns at once.  Buffers must stay alive until the
+ *     stream work completes.
+ *   - Base pointers must be 16-byte aligned.
+ *   - Return value: VLGQA_OK, or an error code; no exception crosses the ABI.
+ *     vlgqa_last_error() then gives "argument: reason" (thread-local, valid
+ *     until the next call on the same thread).  Argument errors are detected
+ *     on the host before any HIP call is made.
+ *   - Empty problems (no batch, no query rows, no heads' work) return VLGQA_OK
+ *     without launching anything.
+ */
+#ifndef VLGQA_H
+#define VLGQA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum vlgqa_status {
+  VLGQA_OK = 0,
+  VLGQA_EINVAL = 1,        /* a bad argument (mirrors InvalidArgument / InvalidShape) */
+  VLGQA_EUNSUPPORTED = 2,  /* head_dim or dtype not compiled (mirrors UnsupportedOperation) */
+  VLGQA_EHIP = 3           /* the HIP runtime reported a launch failure */
+};
+
+/* storage dtypes of q, k, v and out (LSE is always float32) */
+enum vlgqa_dtype { VLGQA_F32 = 0, VLGQA_F16 = 1, VLGQA_BF16 = 2 };
+
+/*
+ * Packed variable-length forward.
+ * boostr 0.2.0, src/ops/traits/attention/varlen_attention.rs,
+ * VarLenAttentionOps::varlen_attention_fwd (layout contract, GQA key/value
+ * head mapping, cumulative sequence lengths; returns output and logsumexp).
+ *
+ *   q            [total_q, num_heads, head_dim]      dtype
+ *   k, v         [total_k, num_kv_heads, head_dim]   dtype
+ *   cu_seqlens_q [batch_size + 1] int32, device: sequence b owns query rows
+ *                cu_seqlens_q[b] .. cu_seqlens_q[b+1]; cu[0] = 0, non-decreasing,
+ *                cu[batch_size] = total_q.  Likewise cu_seqlens_k for k/v.
+ *                The contents are trusted (they are device memory).
+ *   max_seqlen_q / max_seqlen_k  upper bounds of the per-sequence lengths
+ *                (they size the launch; a longer sequence is only partly computed).
+ *   causal       0/1.  There is no window on this entry point.
+ *   out          [total_q, num_heads, head_dim]      dtype
+ *   lse          [total_q, num_heads]                float32, natural log
+ *
+ * Errors: EINVAL for num_heads % num_kv_heads != 0, negative extents, null or
+ * misaligned pointers with non-empty extents; EUNSUPPORTED for head_dim not in
+ * {64, 128} or an unknown dtype.
+ */
+int varlen_attention_fwd(const void* q, const void* k, const void* v,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int64_t total_q, int64_t total_k, int64_t batch_size,
+                         int64_t num_heads, int64_t num_kv_heads,
+                         int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t head_dim,
+                         int causal, int dtype,
+                         void* out, float* lse, void* hip_stream);
+
+/*
+ * Dense forward over a KV buffer that may be longer than the attended part.
+ * boostr, src/ops/traits/attention/flash.rs, FlashAttentionOps::flash_attention_fwd
+ * (layout contract, GQA support, sliding window, kv_seq_len).
+ *
+ *   q      [batch, num_heads, seqlen_q, head_dim]        dtype
+ *   k, v   [batch, num_kv_heads, kv_capacity, head_dim]  dtype; kv_capacity is
+ *          the dim-2 memory stride
+ *   kv_seq_len  number of leading key positions attended (0 <= n <= kv_capacity),
+ *          or < 0 for "None" = kv_capacity.  Positions n .. kv_capacity-1 are
+ *          never read.
+ *   causal 0/1;  window_size 0 = off, W > 0 = only the W most recent keys.
+ *   out    [batch, num_heads, seqlen_q, head_dim]        dtype
+ *   lse    [batch, num_heads, seqlen_q]                  float32
+ *
+ * Errors: EINVAL as above, plus kv_seq_len > kv_capacity and window_size < 0;
+ * EUNSUPPORTED as above.
+ */
+int flash_attention_fwd(const void* q, const void* k, const void* v,
+                        int64_t batch, int64_t num_heads, int64_t num_kv_heads,
+                        int64_t seqlen_q, int64_t kv_capacity, int64_t head_dim,
+                        int causal, int64_t window_size, int64_t kv_seq_len,
+                        int dtype, void* out, float* lse, void* hip_stream);
+
+/*
+ * FP8 (OCP E4M3, "e4m3fn": max 448, no infinities) dense forward.
+ * boostr, src/ops/traits/attention/flash.rs,
+ * FlashAttentionOps::flash_attention_fwd_fp8 (per-tensor scales, FP32
+ * accumulation).
+ *
+ *   q      [batch, num_heads, seqlen_q, head_dim]     uint8 E4M3 codes
+ *   k, v   [batch, num_kv_heads, seqlen_k, head_dim]  uint8 E4M3 codes
+ *   q_scale, k_scale, v_scale  dequantisation: real value = code value * scale
+ *   o_scale                    output quantisation: out = E4M3(O / o_scale),
+ *                              round to nearest even, saturating at +-448
+ *   out    [batch, num_heads, seqlen_q, head_dim]     uint8 E4M3 codes
+ *   lse    [batch, num_heads, seqlen_q]               float32, over the scaled
+ *                              scores q_scale*k_scale*<q8,k8>/sqrt(head_dim)
+ *
+ * Errors: EINVAL as above, plus any scale that is not finite and positive;
+ * EUNSUPPORTED for head_dim not in {64, 128}.
+ */
+int flash_attention_fwd_fp8(const void* q, const void* k, const void* v,
+                            int64_t batch, int64_t num_heads, int64_t num_kv_heads,
+                            int64_t seqlen_q, int64_t seqlen_k, int64_t head_dim,
+                            int causal, float q_scale, float k_scale, float v_scale,
+                            float o_scale, void* out, float* lse, void* hip_stream);
+
+/* "argument: reason" for the last non-OK return on this thread ("" if none). */
+const char* vlgqa_last_error(void);
+
+/* Library version string. */
+const char* vlgqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VLGQA_H */

@@ -355,3 +355,28 @@ def dense_rows(q, k, v, num_heads: int, num_kv_heads: int, causal: bool, samples
         outs.append(o[0])
         lses.append(l[0])
     return np.array(outs), np.array(lses)
+
+
+def fp8_rows(q8, k8, v8, num_heads: int, num_kv_heads: int, causal: bool, samples,
+             q_scale: float, k_scale: float, v_scale: float, o_scale: float):
+    """(o8 codes, O f64, LSE) of the listed (batch b, head h, row i) triples of
+    the FP8 entry point; only the needed slices are decoded."""
+    G = _check_heads(num_heads, num_kv_heads)
+    q8, k8, v8 = as_np(q8), as_np(k8), as_np(v8)
+    D = q8.shape[3]
+    Sq, Sk = q8.shape[2], k8.shape[2]
+    scale = 1.0 / math.sqrt(D)
+    outs, lses = [], []
+    cache = {}
+    for (b, h, i) in samples:
+        kvh = h // G
+        if (b, kvh) not in cache:
+            cache[(b, kvh)] = (_e4m3.decode(k8[b, kvh]) * float(k_scale),
+                               _e4m3.decode(v8[b, kvh]) * float(v_scale))
+        K, V = cache[(b, kvh)]
+        qi = (_e4m3.decode(q8[b, h, i]) * float(q_scale))[None, :]
+        o, l = attend_rows(qi, K, V, np.array([i]), Sq, Sk, causal, 0, scale)
+        outs.append(o[0])
+        lses.append(l[0])
+    O = np.array(outs)
+    return _e4m3.encode(O / float(o_scale)), O, np.array(lses)

@@ -1,0 +1,84 @@
+"""Comparison helpers shared by the GPU parity tests (no attention arithmetic)."""
+
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+# tolerances against the f64 oracle (max absolute error)
+#   f32 storage: O and LSE 1e-4; bf16: O 1e-2, LSE 1e-3 (the stated bounds).
+#   f16: O 4e-3, LSE 1e-3 -- derived: P is rounded to f16 (relative 2^-11) before
+#   P.V and O is stored in f16 (half an ulp is 2^-10 at |O| in [1, 2), 2^-9 at
+#   [2, 4)), so 4e-3 covers both with margin; scores are exact products
+#   accumulated in f32, so LSE errors stay near 1e-5.
+#   E4M3: |o8 * o_scale - O| <= 6e-2 * amax|O| and LSE 1e-3.
+TOL = {
+    torch.float32: (1e-4, 1e-4),
+    torch.bfloat16: (1e-2, 1e-3),
+    torch.float16: (4e-3, 1e-3),
+}
+FP8_REL_TOL = 6e-2
+FP8_LSE_TOL = 1e-3
+
+
+def oracle_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.double().numpy()
+
+
+def assert_close(name, got, ref, tol):
+    """Max-abs comparison; -inf entries must coincide exactly."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert not np.isnan(got).any(), f"{name}: NaN in the result"
+    ninf_ref, ninf_got = np.isneginf(ref), np.isneginf(got)
+    assert (ninf_ref == ninf_got).all(), f"{name}: -inf pattern differs " \
+        f"({int(ninf_ref.sum())} expected, {int(ninf_got.sum())} got)"
+    f = ~ninf_ref
+    if f.any():
+        err = np.abs(got[f] - ref[f])
+        worst = float(err.max())
+        assert worst <= tol, f"{name}: max |err| {worst:.3e} > {tol:.1e} " \
+            f"at {np.unravel_index(int(np.argmax(np.where(f, np.abs(got - np.where(f, ref, 0)), -1))), got.shape)}"
+        return worst
+    return 0.0
+
+
+def e4m3_decode_torch(codes: torch.Tensor) -> np.ndarray:
+    """E4M3 codes -> float64 via torch's own float8 type (not the oracle codec)."""
+    return codes.detach().cpu().view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def sample_rows(rng, lengths, heads, n):
+    """n random (sequence, head, row) triples plus each sequence's first/last rows."""
+    out = []
+    for b, L in enumerate(lengths):
+        if L == 0:
+            continue
+        for h in (0, heads - 1):
+            out += [(b, h, 0), (b, h, L - 1), (b, h, min(L - 1, 127)), (b, h, min(L - 1, 128))]
+    nz = [b for b, L in enumerate(lengths) if L > 0]
+    for _ in range(n):
+        b = int(rng.choice(nz))
+        out.append((b, int(rng.integers(heads)), int(rng.integers(lengths[b]))))
+    return sorted(set(out))
+
+
+def nan_like(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.uint8:
+        return torch.full_like(t, 0x7F)
+    return torch.full_like(t, math.nan)

@@ -1,0 +1,160 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects bad arguments on the host with the documented codes (no GPU call
+is made for any of these)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from variable_length_gqa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vlgqa.h")
+
+EINVAL, EUNSUP = _lib.VLGQA_EINVAL, _lib.VLGQA_EUNSUPPORTED
+BF16, F32 = _lib.VLGQA_BF16, _lib.VLGQA_F32
+A = 0x10000          # a fake, 16-byte-aligned "device" address (never dereferenced)
+MIS = 0x10008        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def err(lib):
+    return lib.vlgqa_last_error().decode()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("varlen_attention_fwd", "flash_attention_fwd", "flash_attention_fwd_fp8",
+              "vlgqa_last_error", "vlgqa_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) <= set(_lib.SIGNATURES)
+    assert lib.vlgqa_version().decode().startswith("vlgqa")
+
+
+def varlen(lib, **kw):
+    a = dict(q=A, k=A, v=A, cq=A, ck=A, tq=940, tk=940, b=3, h=4, hkv=4, mq=512, mk=512, d=64,
+             causal=0, dtype=F32, out=A, lse=A)
+    a.update(kw)
+    return lib.varlen_attention_fwd(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["tq"], a["tk"],
+                                    a["b"], a["h"], a["hkv"], a["mq"], a["mk"], a["d"],
+                                    a["causal"], a["dtype"], a["out"], a["lse"], None)
+
+
+def dense(lib, **kw):
+    a = dict(q=A, k=A, v=A, b=4, h=32, hkv=8, sq=8192, cap=16384, d=128, causal=1, w=4096,
+             n=8192, dtype=BF16, out=A, lse=A)
+    a.update(kw)
+    return lib.flash_attention_fwd(a["q"], a["k"], a["v"], a["b"], a["h"], a["hkv"], a["sq"],
+                                   a["cap"], a["d"], a["causal"], a["w"], a["n"], a["dtype"],
+                                   a["out"], a["lse"], None)
+
+
+def fp8(lib, **kw):
+    a = dict(q=A, k=A, v=A, b=8, h=32, hkv=8, sq=4096, sk=4096, d=128, causal=1, qs=0.01,
+             ks=0.01, vs=0.01, os=0.01, out=A, lse=A)
+    a.update(kw)
+    return lib.flash_attention_fwd_fp8(a["q"], a["k"], a["v"], a["b"], a["h"], a["hkv"], a["sq"],
+                                       a["sk"], a["d"], a["causal"], a["qs"], a["ks"], a["vs"],
+                                       a["os"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code,arg", [
+    (dict(h=6, hkv=4), EINVAL, "num_heads"),
+    (dict(h=0), EINVAL, "num_heads"),
+    (dict(hkv=0), EINVAL, "num_kv_heads"),
+    (dict(d=96), EUNSUP, "head_dim"),
+    (dict(d=256), EUNSUP, "head_dim"),
+    (dict(dtype=7), EUNSUP, "dtype"),
+    (dict(tq=-1), EINVAL, "total_q"),
+    (dict(b=-2), EINVAL, "batch_size"),
+    (dict(mq=-1), EINVAL, "max_seqlen_q"),
+    (dict(causal=2), EINVAL, "causal"),
+    (dict(q=0), EINVAL, "q"),
+    (dict(k=MIS), EINVAL, "k"),
+    (dict(cq=0), EINVAL, "cu_seqlens_q"),
+    (dict(ck=MIS), EINVAL, "cu_seqlens_k"),
+    (dict(out=0), EINVAL, "out"),
+    (dict(lse=MIS), EINVAL, "lse"),
+    (dict(tq=1 << 31), EINVAL, "total_q"),
+])
+def test_varlen_rejects(lib, kw, code, arg):
+    assert varlen(lib, **kw) == code
+    assert err(lib).startswith(arg + ":"), err(lib)
+
+
+def test_varlen_empty_problems_return_ok_without_pointers(lib):
+    assert varlen(lib, b=0, q=0, k=0, v=0, cq=0, ck=0, out=0, lse=0) == _lib.VLGQA_OK
+    assert varlen(lib, tq=0, q=0, k=0, v=0, cq=0, ck=0, out=0, lse=0) == _lib.VLGQA_OK
+    assert varlen(lib, mq=0, q=0, k=0, v=0, cq=0, ck=0, out=0, lse=0) == _lib.VLGQA_OK
+    assert err(lib) == ""
+
+
+@pytest.mark.parametrize("kw,code,arg", [
+    (dict(n=16385), EINVAL, "kv_seq_len"),
+    (dict(w=-1), EINVAL, "window_size"),
+    (dict(h=32, hkv=5), EINVAL, "num_heads"),
+    (dict(d=32), EUNSUP, "head_dim"),
+    (dict(sq=-5), EINVAL, "seqlen_q"),
+    (dict(cap=-1), EINVAL, "kv_capacity"),
+    (dict(b=-1), EINVAL, "batch"),
+    (dict(v=0), EINVAL, "v"),
+    (dict(q=MIS), EINVAL, "q"),
+    (dict(dtype=-1), EUNSUP, "dtype"),
+])
+def test_dense_rejects(lib, kw, code, arg):
+    assert dense(lib, **kw) == code
+    assert err(lib).startswith(arg + ":"), err(lib)
+
+
+def test_dense_empty_problems_return_ok(lib):
+    assert dense(lib, b=0, q=0, k=0, v=0, out=0, lse=0) == _lib.VLGQA_OK
+    assert dense(lib, sq=0, q=0, k=0, v=0, out=0, lse=0) == _lib.VLGQA_OK
+
+
+@pytest.mark.parametrize("kw,arg", [
+    (dict(qs=0.0), "q_scale"), (dict(ks=-1.0), "k_scale"), (dict(vs=float("nan")), "v_scale"),
+    (dict(os=float("inf")), "o_scale"), (dict(qs=1e-30, ks=1e-30), "q_scale"),
+    (dict(h=4, hkv=3), "num_heads"), (dict(sk=-1), "kv_capacity"),
+])
+def test_fp8_rejects(lib, kw, arg):
+    assert fp8(lib, **kw) == EINVAL
+    assert err(lib).startswith(arg + ":"), err(lib)
+
+
+def test_fp8_unsupported_head_dim(lib):
+    assert fp8(lib, d=80) == EUNSUP
+
+
+def test_python_binding_raises_without_touching_gpu():
+    import torch
+
+    import variable_length_gqa_amd as vg
+
+    q = torch.zeros(4, 2, 64)
+    with pytest.raises(ValueError):
+        vg.varlen_attention_fwd(q, q, q, torch.zeros(2, dtype=torch.int32),
+                                torch.zeros(2, dtype=torch.int32), 1, 2, 2, 4, 4, 64, False)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,671 @@
+// Fused attention forward for gfx950 (CDNA4): packed varlen and dense layouts,
+// GQA, causal / sliding-window masks, bf16 / f16 / f32 / E4M3 storage.
+//
+// What is computed (boostr varlen_attention.rs "VarLenAttentionOps" and boostr
+// flash.rs "FlashAttentionOps"): for each (sequence, query head h, query row i)
+// O_i = softmax(scale * q_i K^T restricted to the visible keys) V with
+// kv_head = h / (H / Hkv), plus LSE_i = ln sum exp(scores) in f32.  The
+// evaluation is the tiled online softmax of realizar attention.rs IMP-111
+// ("tiled_single_head_attention"): per query row a running maximum, running
+// denominator and running weighted sum, rescaled when the maximum grows.
+//
+// Work decomposition: one workgroup = one (sequence, 128-row query tile, query
+// head); 4 waves x 32 query rows.  K/V tiles of 64 keys are staged through LDS
+// (double buffered, one barrier per tile) and shared by the 4 waves.
+//
+// Matrix-core formulation (v_mfma_f32_32x32x16_{bf16,f16}, wave64):
+//   S^T = K Q^T   A = K tile (32 keys x 16 d, from LDS), B = Q^T (registers)
+//                 -> lane l holds query (l % 32) and 16 of the 32 keys of a
+//                    32-key block, so a row's max / sum is an in-lane
+//                    reduction plus one permlane32 swap.
+//   O^T = V^T P^T A = V^T (32 d x 16 keys, LDS holds V transposed),
+//                 B = P^T taken straight from the S^T accumulator registers
+//                 (converted to 16 bit) -> O^T keeps query (l % 32) per lane,
+//                 so the per-row rescale factor is a per-lane scalar.
+// The P registers cover keys {0-3, 8-11} (lanes 0-31) and {4-7, 12-15}
+// (lanes 32-63) of each 16-key step; V^T is written to LDS with the middle two
+// 4-key quads of every 16 keys swapped so that each lane reads its 8 keys as
+// one 16-byte vector.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fwd_params.h"
+
+namespace vlgqa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// a row's reference maximum is only moved when a tile raises it by more than
+// this (log2 units); until then probabilities may reach 2^kRescaleSlack.  The
+// result is exact either way: numerator and denominator use the same reference.
+constexpr float kRescaleSlack = 8.0f;
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float swap_halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
+template <int ELEM>
+__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (ELEM == E_F16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else {  // bf16, and E4M3 widened to bf16
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+}
+
+// two floats -> packed 16-bit pair (round to nearest even)
+template <int ELEM>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (ELEM == E_F16) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  } else {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+}
+
+// OCP E4M3 code (low 8 bits of c) -> bf16 bits, exact.  NaN codes map to NaN.
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 8;
+  uint32_t em = c & 0x7Fu;
+  uint32_t normal = (em + (120u << 3)) << 4;                       // exponent e -> e + 120
+  uint32_t sub = __float_as_uint((float)em * 0.001953125f) >> 16;  // m * 2^-9, exact in bf16
+  uint32_t r = em >= 8u ? normal : sub;
+  r = em == 0x7Fu ? 0x7FC0u : r;
+  return s | r;
+}
+
+// 4 E4M3 codes (one u32) -> 4 bf16 (two u32)
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+  u32x2 r;
+  r[0] = e4m3_to_bf16(w & 0xFF) | (e4m3_to_bf16((w >> 8) & 0xFF) << 16);
+  r[1] = e4m3_to_bf16((w >> 16) & 0xFF) | (e4m3_to_bf16(w >> 24) << 16);
+  return r;
+}
+
+// f32 -> OCP E4M3 code, round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t s = (u >> 24) & 0x80u;
+  float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.0f) return s | 0x7Eu;
+  if (a < 0.015625f) {  // subnormal range: spacing 2^-9 (8 lands on the smallest normal)
+    return s | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  uint32_t ua = __float_as_uint(a);
+  ua += 0x7FFFFu + ((ua >> 20) & 1u);  // round the f32 mantissa to 3 bits, ties to even
+  uint32_t e = (ua >> 23) - 120u;      // e4m3 exponent field (bias 7)
+  uint32_t m = (ua >> 20) & 7u;
+  if (e > 15u || (e == 15u && m == 7u)) return s | 0x7Eu;
+  return s | (e << 3) | m;
+}
+
+// ---------------------------------------------------------------------------
+// work decode: XCD-aware, longest query tiles first
+// ---------------------------------------------------------------------------
+//
+// Workgroups are handed to the 8 XCDs round-robin (block i -> XCD i % 8).  A
+// "group" is (query tile, sequence, kv head); its G query heads read the same
+// K/V, so they are placed on consecutive slots of ONE XCD and share its L2.
+// Groups are ordered by descending query tile: under a causal mask later
+// tiles see more keys, so the longest work is dispatched first.
+struct Work {
+  int b, h, kvh, r0;
+  int q_start, Lq, k_start, Lk;
+};
+
+__device__ __forceinline__ bool decode_work(const FwdParams& p, Work& w) {
+  const int G = p.group;
+  const int pid = blockIdx.x;
+  const int xcd = pid & 7;
+  const int slot = pid >> 3;
+  const int gq = slot / G;
+  const int g = slot - gq * G;
+  const int grp = gq * 8 + xcd;
+  if (grp >= p.n_groups) return false;
+  w.kvh = grp % p.kv_heads;
+  const int t2 = grp / p.kv_heads;
+  w.b = t2 % p.batch;
+  const int tidx = t2 / p.batch;
+  w.r0 = (p.n_qtiles - 1 - tidx) * kBlockM;
+  w.h = w.kvh * G + g;
+  w.q_start = 0;
+  w.Lq = p.seqlen_q;
+  w.k_start = 0;
+  w.Lk = p.seqlen_k;
+  if (p.cu_q) {
+    w.q_start = p.cu_q[w.b];
+    w.Lq = p.cu_q[w.b + 1] - w.q_start;
+  }
+  if (p.cu_k) {
+    w.k_start = p.cu_k[w.b];
+    w.Lk = p.cu_k[w.b + 1] - w.k_start;
+  }
+  return w.r0 < w.Lq;
+}
+
+// ---------------------------------------------------------------------------
+// per-lane online-softmax state and the shared pieces of the tile loop
+// ---------------------------------------------------------------------------
+
+template <int NOB>
+struct RowState {
+  float m;         // reference maximum, log2 domain (score * score_mul)
+  float l;         // this lane's half of the running denominator
+  f32x16 o[NOB];   // O^T accumulators: query (lane % 32), 16 d values per block
+};
+
+// Mask the S^T accumulators of a 64-key tile starting at key c0 for the
+// lane's query row q.  Key of register r in block kb: c0 + 32 kb + 8 (r / 4)
+// + 4 (lane / 32) + r % 4.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int c0, int hl, int q, int off, int Lk,
+                                          bool upper, int window) {
+  const int hi = upper ? min(Lk - 1, q + off) : Lk - 1;
+  const int lo = window > 0 ? q + off - window + 1 : 0;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = c0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+      if (key > hi || key < lo) s[kb][r] = -INFINITY;
+    }
+  }
+}
+
+// One online-softmax step over the 64 scores of this lane's row (2 blocks x 16
+// registers, the other 32 scores of the row live in lane ^ 32).  Leaves the
+// probabilities (relative to the reference maximum) in s.  EXACT rounds
+// score * mul before subtracting the reference, so the maximal score maps to
+// exactly exp2(0) = 1 (one more VALU op per score; used by the f32 kernel).
+template <int NOB, bool EXACT = false>
+__device__ __forceinline__ void softmax_step(f32x16 (&s)[2], RowState<NOB>& st, float mul) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+  mx = swap_halves_max(mx) * mul;  // -inf stays -inf
+  const bool up = mx > st.m + kRescaleSlack;  // st.m = -inf: any finite maximum moves it
+  if (wave_any(up)) {
+    const float alpha = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.0f;
+    st.m = up ? mx : st.m;
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < NOB; ++i) st.o[i] *= alpha;
+  }
+  const float ref = st.m == -INFINITY ? 0.0f : st.m;
+  float sum = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float arg;
+      if constexpr (EXACT) {
+#pragma clang fp contract(off)
+        const float t = s[kb][r] * mul;  // rounded on its own, not fused into the subtraction
+        arg = t - ref;
+      } else {
+        arg = __builtin_fmaf(s[kb][r], mul, -ref);
+      }
+      const float pr = __builtin_amdgcn_exp2f(arg);
+      s[kb][r] = pr;
+      sum += pr;
+    }
+  }
+  st.l += sum;
+}
+
+// Normalise and store O (rows of the lane's query, 4 consecutive d per store)
+// and LSE.  OUT_ELEM selects the storage conversion.
+template <int OUT_ELEM, int D>
+__device__ __forceinline__ void store_rows(const FwdParams& p, const Work& w, int qrow, int hl,
+                                           RowState<D / 32>& st) {
+  const float ltot = swap_halves_sum(st.l);
+  if (qrow >= w.Lq) return;
+  const float inv = ltot > 0.0f ? p.out_mul / ltot : 0.0f;
+  const int64_t orow = (int64_t)w.b * p.o_bs + (int64_t)(w.q_start + qrow) * p.o_rs +
+                       (int64_t)w.h * p.o_hs;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + g * 8 + 4 * hl;
+      const float x0 = st.o[db][4 * g + 0] * inv, x1 = st.o[db][4 * g + 1] * inv;
+      const float x2 = st.o[db][4 * g + 2] * inv, x3 = st.o[db][4 * g + 3] * inv;
+      if constexpr (OUT_ELEM == E_F32) {
+        f32x4 v = {x0, x1, x2, x3};
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d0) = v;
+      } else if constexpr (OUT_ELEM == E_E4M3) {
+        uint32_t v = f32_to_e4m3(x0) | (f32_to_e4m3(x1) << 8) | (f32_to_e4m3(x2) << 16) |
+                     (f32_to_e4m3(x3) << 24);
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.o) + orow + d0) = v;
+      } else {
+        u32x2 v = {pack2<OUT_ELEM>(x0, x1), pack2<OUT_ELEM>(x2, x3)};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.o) + orow + d0) = v;
+      }
+    }
+  }
+  if (hl == 0) {
+    const float lse = ltot > 0.0f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -INFINITY;
+    p.lse[(int64_t)w.b * p.l_bs + (int64_t)(w.q_start + qrow) * p.l_rs + (int64_t)w.h * p.l_hs] = lse;
+  }
+}
+
+// Key range [lo, hi) visible to query rows [qa, qb] of a sequence.
+__device__ __forceinline__ void key_range(const FwdParams& p, const Work& w, int qa, int qb,
+                                          int& lo, int& hi) {
+  const int off = w.Lk - w.Lq;
+  const bool upper = p.causal || p.window > 0;
+  hi = upper ? min(w.Lk, qb + off + 1) : w.Lk;
+  lo = p.window > 0 ? max(0, qa + off - p.window + 1) : 0;
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit compute kernel (bf16, f16, and E4M3 widened to bf16 on the way in)
+// ---------------------------------------------------------------------------
+
+template <int ELEM, int D>
+struct Tile16 {
+  static constexpr int KP = D + 8;          // K row pitch in LDS (u16), 16 B pad
+  static constexpr int VP = kBlockN + 8;    // V^T row pitch in LDS (u16)
+  static constexpr int EB = ELEM == E_E4M3 ? 1 : 2;  // stored bytes per element
+  // K: 16-byte global chunks
+  static constexpr int K_CPR = D * EB / 16;                   // chunks per key row
+  static constexpr int K_CPT = kBlockN * K_CPR / kThreads;    // chunks per thread
+  // V: units of 4 keys x 8 d
+  static constexpr int V_UNITS = (kBlockN / 4) * (D / 8);
+  static_assert(K_CPT >= 1 && V_UNITS <= kThreads, "tile shape");
+};
+
+template <int ELEM, int D>
+struct Staging16 {
+  u32x4 k[Tile16<ELEM, D>::K_CPT];
+  u32x4 v[4];  // 4 key rows x 8 d (E4M3: only the low 2 words used)
+};
+
+template <int ELEM, int D>
+__device__ __forceinline__ void load_tile16(const FwdParams& p, const Work& w, int c0, int tid,
+                                            Staging16<ELEM, D>& st) {
+  using T = Tile16<ELEM, D>;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) +
+                         ((int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs + (int64_t)w.kvh * p.k_hs) * T::EB;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) +
+                         ((int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs + (int64_t)w.kvh * p.k_hs) * T::EB;
+  const int64_t rs = p.k_rs * T::EB;
+#pragma unroll
+  for (int c = 0; c < T::K_CPT; ++c) {
+    const int idx = c * kThreads + tid;
+    const int row = idx / T::K_CPR, col = idx % T::K_CPR;
+    const int key = c0 + row;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (key < w.Lk) z = *reinterpret_cast<const u32x4*>(kbase + key * rs + col * 16);
+    st.k[c] = z;
+  }
+  if (tid < T::V_UNITS) {
+    const int db = tid % (D / 8), kq = tid / (D / 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = c0 + 4 * kq + j;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (key < w.Lk) {
+        if constexpr (T::EB == 2) {
+          z = *reinterpret_cast<const u32x4*>(vbase + key * rs + db * 16);
+        } else {
+          u32x2 t = *reinterpret_cast<const u32x2*>(vbase + key * rs + db * 8);
+          z[0] = t[0];
+          z[1] = t[1];
+        }
+      }
+      st.v[j] = z;
+    }
+  }
+}
+
+template <int ELEM, int D>
+__device__ __forceinline__ void store_tile16(uint16_t* sK, uint16_t* sV, int tid,
+                                             const Staging16<ELEM, D>& st) {
+  using T = Tile16<ELEM, D>;
+#pragma unroll
+  for (int c = 0; c < T::K_CPT; ++c) {
+    const int idx = c * kThreads + tid;
+    const int row = idx / T::K_CPR, col = idx % T::K_CPR;
+    if constexpr (T::EB == 2) {
+      *reinterpret_cast<u32x4*>(sK + row * T::KP + col * 8) = st.k[c];
+    } else {  // 16 codes -> 16 bf16
+      u32x2 a = e4m3x4_to_bf16(st.k[c][0]), b = e4m3x4_to_bf16(st.k[c][1]);
+      u32x2 e = e4m3x4_to_bf16(st.k[c][2]), f = e4m3x4_to_bf16(st.k[c][3]);
+      u32x4 lo = {a[0], a[1], b[0], b[1]}, hi = {e[0], e[1], f[0], f[1]};
+      *reinterpret_cast<u32x4*>(sK + row * T::KP + col * 16) = lo;
+      *reinterpret_cast<u32x4*>(sK + row * T::KP + col * 16 + 8) = hi;
+    }
+  }
+  if (tid < T::V_UNITS) {
+    const int db = tid % (D / 8), kq = tid / (D / 8);
+    // rows j = 0..3 (keys 4kq + j) as 8 x 16-bit each: w[j][i] holds d = 2i, 2i+1
+    uint32_t w[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (T::EB == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[j][i] = st.v[j][i];
+      } else {
+        u32x2 a = e4m3x4_to_bf16(st.v[j][0]), b = e4m3x4_to_bf16(st.v[j][1]);
+        w[j][0] = a[0]; w[j][1] = a[1]; w[j][2] = b[0]; w[j][3] = b[1];
+      }
+    }
+    // key quad kq of the tile -> LDS position quad (middle quads of each 16 swapped)
+    const int qq = kq & 3;
+    const int pq = (kq & ~3) | (qq == 1 ? 2 : (qq == 2 ? 1 : qq));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // d = db*8 + 2i: low halves; d = db*8 + 2i + 1: high halves
+      u32x2 ev, od;
+      ev[0] = __builtin_amdgcn_perm(w[1][i], w[0][i], 0x05040100u);
+      ev[1] = __builtin_amdgcn_perm(w[3][i], w[2][i], 0x05040100u);
+      od[0] = __builtin_amdgcn_perm(w[1][i], w[0][i], 0x07060302u);
+      od[1] = __builtin_amdgcn_perm(w[3][i], w[2][i], 0x07060302u);
+      *reinterpret_cast<u32x2*>(sV + (db * 8 + 2 * i) * T::VP + pq * 4) = ev;
+      *reinterpret_cast<u32x2*>(sV + (db * 8 + 2 * i + 1) * T::VP + pq * 4) = od;
+    }
+  }
+}
+
+template <int ELEM, int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void fwd16_kernel(FwdParams p) {
+  using T = Tile16<ELEM, D>;
+  constexpr int NS = D / 16;   // MFMA k-steps over d
+  constexpr int NOB = D / 32;  // O^T accumulator blocks
+  constexpr int OUT = ELEM;    // output stored in the input format
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlockN * T::KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * T::VP];
+
+  Work w;
+  if (!decode_work(p, w)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;
+  const int qrow = w.r0 + wid * 32 + ql;  // this lane's query row within the sequence
+
+  // Q^T fragments: lane holds q[qrow][16 s + 8 hl .. +8]
+  u32x4 qf[NS];
+  {
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(p.q) +
+                        ((int64_t)w.b * p.q_bs + (int64_t)(w.q_start + qrow) * p.q_rs +
+                         (int64_t)w.h * p.q_hs) * T::EB;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (qrow < w.Lq) {
+        if constexpr (T::EB == 2) {
+          z = *reinterpret_cast<const u32x4*>(qb + (16 * s + 8 * hl) * 2);
+        } else {
+          u32x2 c = *reinterpret_cast<const u32x2*>(qb + 16 * s + 8 * hl);
+          u32x2 a = e4m3x4_to_bf16(c[0]), bb = e4m3x4_to_bf16(c[1]);
+          z[0] = a[0]; z[1] = a[1]; z[2] = bb[0]; z[3] = bb[1];
+        }
+      }
+      qf[s] = z;
+    }
+  }
+
+  RowState<NOB> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NOB; ++i) st.o[i] = f32x16{};
+
+  const int rlast = min(w.r0 + kBlockM, w.Lq) - 1;
+  int kv_lo, kv_hi;
+  key_range(p, w, w.r0, rlast, kv_lo, kv_hi);
+  // this wave's rows and keys
+  const int wa = w.r0 + wid * 32, wb = min(w.r0 + wid * 32 + 31, w.Lq - 1);
+  int wlo, whi;
+  key_range(p, w, wa, wb, wlo, whi);
+  const bool wave_live = wa <= wb;
+  const int off = w.Lk - w.Lq;
+  const bool upper = p.causal || p.window > 0;
+
+  const int t0 = kv_lo / kBlockN;
+  const int t1 = kv_hi > kv_lo ? (kv_hi + kBlockN - 1) / kBlockN : t0;
+
+  Staging16<ELEM, D> stg;
+  if (t0 < t1) load_tile16<ELEM, D>(p, w, t0 * kBlockN, tid, stg);
+
+  for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    uint16_t* k_s = sK[buf];
+    uint16_t* v_s = sV[buf];
+    store_tile16<ELEM, D>(k_s, v_s, tid, stg);
+    __syncthreads();
+    if (t + 1 < t1) load_tile16<ELEM, D>(p, w, (t + 1) * kBlockN, tid, stg);
+
+    const int c0 = t * kBlockN;
+    if (!wave_live || c0 >= whi || c0 + kBlockN <= wlo) continue;
+
+    // S^T = K Q^T for two 32-key blocks
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(k_s + ql * T::KP + 16 * ks + 8 * hl);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(k_s + (32 + ql) * T::KP + 16 * ks + 8 * hl);
+      s[0] = mfma16<ELEM>(a0, qf[ks], s[0]);
+      s[1] = mfma16<ELEM>(a1, qf[ks], s[1]);
+    }
+
+    const bool need_mask = (c0 + kBlockN > w.Lk) || (upper && c0 + kBlockN - 1 > wa + off) ||
+                           (p.window > 0 && c0 < wb + off - p.window + 1);
+    if (need_mask) mask_tile(s, c0, hl, qrow, off, w.Lk, upper, p.window);
+
+    softmax_step<NOB>(s, st, p.score_mul);
+
+    // P^T operands: step t2 uses registers 8 (t2 % 2) .. +7 of block t2 / 2
+    u32x4 pk[4];
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2) {
+      const f32x16& sb = s[t2 >> 1];
+      const int r = 8 * (t2 & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[t2][i] = pack2<ELEM>(sb[r + 2 * i], sb[r + 2 * i + 1]);
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2) {
+#pragma unroll
+      for (int db = 0; db < NOB; ++db) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(v_s + (db * 32 + ql) * T::VP + 16 * t2 + 8 * hl);
+        st.o[db] = mfma16<ELEM>(a, pk[t2], st.o[db]);
+      }
+    }
+  }
+
+  store_rows<OUT, D>(p, w, qrow, hl, st);
+}
+
+// ---------------------------------------------------------------------------
+// f32 kernel (v_mfma_f32_32x32x2_f32: exact products, f32 accumulation)
+// ---------------------------------------------------------------------------
+//
+// The d contraction order is permuted consistently for Q and K: MFMA step s,
+// lane half h <-> d = (D/2) h + s, so each lane reads contiguous d values.
+// P.V: step r of key block kb pairs the keys 32 kb + 8 (r/4) + 4 h + r%4
+// (h = lane half), which is exactly what accumulator register r holds, so P
+// needs no movement and V stays row-major in LDS.
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 2)))
+void fwd32_kernel(FwdParams p) {
+  constexpr int P32 = D + 4;  // LDS row pitch (floats)
+  constexpr int NOB = D / 32;
+  constexpr int CPR = D / 4;                      // 16-byte chunks per row
+  constexpr int CPT = kBlockN * CPR / kThreads;   // per thread, per tensor
+  __shared__ __attribute__((aligned(16))) float sK[2][kBlockN * P32];
+  __shared__ __attribute__((aligned(16))) float sV[2][kBlockN * P32];
+
+  Work w;
+  if (!decode_work(p, w)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int hl = lane >> 5, ql = lane & 31;
+  const int qrow = w.r0 + wid * 32 + ql;
+
+  float qf[D / 2];
+  {
+    const float* qb = reinterpret_cast<const float*>(p.q) + (int64_t)w.b * p.q_bs +
+                      (int64_t)(w.q_start + qrow) * p.q_rs + (int64_t)w.h * p.q_hs + (D / 2) * hl;
+#pragma unroll
+    for (int s = 0; s < D / 2; s += 4) {
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      if (qrow < w.Lq) z = *reinterpret_cast<const f32x4*>(qb + s);
+      qf[s] = z[0]; qf[s + 1] = z[1]; qf[s + 2] = z[2]; qf[s + 3] = z[3];
+    }
+  }
+
+  RowState<NOB> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NOB; ++i) st.o[i] = f32x16{};
+
+  const int rlast = min(w.r0 + kBlockM, w.Lq) - 1;
+  int kv_lo, kv_hi;
+  key_range(p, w, w.r0, rlast, kv_lo, kv_hi);
+  const int wa = w.r0 + wid * 32, wb = min(w.r0 + wid * 32 + 31, w.Lq - 1);
+  int wlo, whi;
+  key_range(p, w, wa, wb, wlo, whi);
+  const bool wave_live = wa <= wb;
+  const int off = w.Lk - w.Lq;
+  const bool upper = p.causal || p.window > 0;
+  const int t0 = kv_lo / kBlockN;
+  const int t1 = kv_hi > kv_lo ? (kv_hi + kBlockN - 1) / kBlockN : t0;
+
+  const float* kbase = reinterpret_cast<const float*>(p.k) + (int64_t)w.b * p.k_bs +
+                       (int64_t)w.k_start * p.k_rs + (int64_t)w.kvh * p.k_hs;
+  const float* vbase = reinterpret_cast<const float*>(p.v) + (int64_t)w.b * p.k_bs +
+                       (int64_t)w.k_start * p.k_rs + (int64_t)w.kvh * p.k_hs;
+  f32x4 rk[CPT], rv[CPT];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = c * kThreads + tid, row = idx / CPR, col = idx % CPR;
+      const int key = c0 + row;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f}, bb = {0.f, 0.f, 0.f, 0.f};
+      if (key < w.Lk) {
+        a = *reinterpret_cast<const f32x4*>(kbase + (int64_t)key * p.k_rs + col * 4);
+        bb = *reinterpret_cast<const f32x4*>(vbase + (int64_t)key * p.k_rs + col * 4);
+      }
+      rk[c] = a;
+      rv[c] = bb;
+    }
+  };
+  if (t0 < t1) load(t0 * kBlockN);
+
+  for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    float* k_s = sK[buf];
+    float* v_s = sV[buf];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = c * kThreads + tid, row = idx / CPR, col = idx % CPR;
+      *reinterpret_cast<f32x4*>(k_s + row * P32 + col * 4) = rk[c];
+      *reinterpret_cast<f32x4*>(v_s + row * P32 + col * 4) = rv[c];
+    }
+    __syncthreads();
+    if (t + 1 < t1) load((t + 1) * kBlockN);
+
+    const int c0 = t * kBlockN;
+    if (!wave_live || c0 >= whi || c0 + kBlockN <= wlo) continue;
+
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ks += 4) {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(k_s + ql * P32 + (D / 2) * hl + ks);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(k_s + (32 + ql) * P32 + (D / 2) * hl + ks);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[e], qf[ks + e], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[e], qf[ks + e], s[1], 0, 0, 0);
+      }
+    }
+
+    const bool need_mask = (c0 + kBlockN > w.Lk) || (upper && c0 + kBlockN - 1 > wa + off) ||
+                           (p.window > 0 && c0 < wb + off - p.window + 1);
+    if (need_mask) mask_tile(s, c0, hl, qrow, off, w.Lk, upper, p.window);
+
+    softmax_step<NOB, true>(s, st, p.score_mul);
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+#pragma unroll
+        for (int db = 0; db < NOB; ++db) {
+          const float a = v_s[key * P32 + db * 32 + ql];
+          st.o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][r], st.o[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  store_rows<E_F32, D>(p, w, qrow, hl, st);
+}
+
+// ---------------------------------------------------------------------------
+// host launch
+// ---------------------------------------------------------------------------
+
+hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t stream) {
+  const int64_t grid = fwd_grid_size(p);
+  if (grid <= 0) return hipSuccess;
+  const dim3 g((unsigned)grid), b(kThreads);
+#define VLGQA_LAUNCH(KERNEL) hipLaunchKernelGGL((KERNEL), g, b, 0, stream, p)
+  if (head_dim == 128) {
+    switch (elem) {
+      case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 128>)); break;
+      case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 128>)); break;
+      case E_E4M3: VLGQA_LAUNCH((fwd16_kernel<E_E4M3, 128>)); break;
+      case E_F32: VLGQA_LAUNCH((fwd32_kernel<128>)); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (head_dim == 64) {
+    switch (elem) {
+      case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 64>)); break;
+      case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 64>)); break;
+      case E_E4M3: VLGQA_LAUNCH((fwd16_kernel<E_E4M3, 64>)); break;
+      case E_F32: VLGQA_LAUNCH((fwd32_kernel<64>)); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef VLGQA_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace vlgqa

@@ -1,0 +1,207 @@
+// C ABI of the attention forward library: argument validation, layout
+// description and dispatch.  The contract of every entry point is documented
+// in include/vlgqa.h.  All checks run on the host before any HIP call, so a
+// rejected call never touches the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "fwd_params.h"
+#include "vlgqa.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* arg, const std::string& reason) {
+  g_last_error = std::string(arg) + ": " + reason;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// non-null and 16-byte aligned
+int check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(VLGQA_EINVAL, name, "null pointer");
+  if (!aligned16(p)) return fail(VLGQA_EINVAL, name, "not 16-byte aligned");
+  return VLGQA_OK;
+}
+
+int check_heads(int64_t num_heads, int64_t num_kv_heads) {
+  if (num_heads <= 0) return fail(VLGQA_EINVAL, "num_heads", "must be positive");
+  if (num_kv_heads <= 0) return fail(VLGQA_EINVAL, "num_kv_heads", "must be positive");
+  if (num_heads % num_kv_heads != 0)
+    return fail(VLGQA_EINVAL, "num_heads", "must be a multiple of num_kv_heads (GQA)");
+  if (num_heads > (1 << 20)) return fail(VLGQA_EINVAL, "num_heads", "too large");
+  return VLGQA_OK;
+}
+
+int check_head_dim(int64_t head_dim) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(VLGQA_EUNSUPPORTED, "head_dim", "only 64 and 128 are compiled");
+  return VLGQA_OK;
+}
+
+int elem_of_dtype(int dtype, int* elem) {
+  switch (dtype) {
+    case VLGQA_F32: *elem = vlgqa::E_F32; return VLGQA_OK;
+    case VLGQA_F16: *elem = vlgqa::E_F16; return VLGQA_OK;
+    case VLGQA_BF16: *elem = vlgqa::E_BF16; return VLGQA_OK;
+    default: return fail(VLGQA_EUNSUPPORTED, "dtype", "unknown dtype code");
+  }
+}
+
+// query tiles / groups / grid must fit the kernel's 32-bit work decode
+int finish_and_launch(vlgqa::FwdParams& p, int64_t max_seqlen_q, int elem, int64_t head_dim,
+                      void* hip_stream) {
+  const int64_t n_qtiles = (max_seqlen_q + vlgqa::kBlockM - 1) / vlgqa::kBlockM;
+  const int64_t n_groups = n_qtiles * p.batch * p.kv_heads;
+  if (n_groups > INT32_MAX / 8 || n_groups * p.group > (int64_t)UINT32_MAX / 2)
+    return fail(VLGQA_EINVAL, "max_seqlen_q", "problem too large for one launch");
+  p.n_qtiles = (int32_t)n_qtiles;
+  p.n_groups = (int32_t)n_groups;
+  hipError_t e = vlgqa::launch_fwd(p, elem, (int)head_dim, reinterpret_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
+  return VLGQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vlgqa_last_error(void) { return g_last_error.c_str(); }
+
+const char* vlgqa_version(void) { return "vlgqa 0.1.0 gfx950"; }
+
+int varlen_attention_fwd(const void* q, const void* k, const void* v,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int64_t total_q, int64_t total_k, int64_t batch_size,
+                         int64_t num_heads, int64_t num_kv_heads,
+                         int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t head_dim,
+                         int causal, int dtype, void* out, float* lse, void* hip_stream) {
+  g_last_error.clear();
+  int rc, elem = 0;
+  if ((rc = elem_of_dtype(dtype, &elem))) return rc;
+  if ((rc = check_head_dim(head_dim))) return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads))) return rc;
+  if (total_q < 0) return fail(VLGQA_EINVAL, "total_q", "must be non-negative");
+  if (total_k < 0) return fail(VLGQA_EINVAL, "total_k", "must be non-negative");
+  if (batch_size < 0) return fail(VLGQA_EINVAL, "batch_size", "must be non-negative");
+  if (max_seqlen_q < 0) return fail(VLGQA_EINVAL, "max_seqlen_q", "must be non-negative");
+  if (max_seqlen_k < 0) return fail(VLGQA_EINVAL, "max_seqlen_k", "must be non-negative");
+  if (causal != 0 && causal != 1) return fail(VLGQA_EINVAL, "causal", "must be 0 or 1");
+  if (total_q > INT32_MAX || total_k > INT32_MAX)
+    return fail(VLGQA_EINVAL, "total_q", "token counts must fit I32 cu_seqlens");
+  if (batch_size > INT32_MAX - 1) return fail(VLGQA_EINVAL, "batch_size", "too large");
+  if (batch_size == 0 || total_q == 0 || max_seqlen_q == 0) return VLGQA_OK;
+  if ((rc = check_ptr(q, "q"))) return rc;
+  if (total_k > 0) {
+    if ((rc = check_ptr(k, "k"))) return rc;
+    if ((rc = check_ptr(v, "v"))) return rc;
+  }
+  if ((rc = check_ptr(cu_seqlens_q, "cu_seqlens_q"))) return rc;
+  if ((rc = check_ptr(cu_seqlens_k, "cu_seqlens_k"))) return rc;
+  if ((rc = check_ptr(out, "out"))) return rc;
+  if ((rc = check_ptr(lse, "lse"))) return rc;
+
+  vlgqa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+  p.q_bs = 0; p.q_rs = num_heads * head_dim; p.q_hs = head_dim;
+  p.k_bs = 0; p.k_rs = num_kv_heads * head_dim; p.k_hs = head_dim;
+  p.o_bs = 0; p.o_rs = num_heads * head_dim; p.o_hs = head_dim;
+  p.l_bs = 0; p.l_rs = num_heads; p.l_hs = 1;
+  p.batch = (int32_t)batch_size;
+  p.heads = (int32_t)num_heads;
+  p.kv_heads = (int32_t)num_kv_heads;
+  p.group = (int32_t)(num_heads / num_kv_heads);
+  p.seqlen_q = 0; p.seqlen_k = 0;
+  p.causal = causal; p.window = 0;
+  p.score_mul = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  p.out_mul = 1.0f;
+  return finish_and_launch(p, max_seqlen_q, elem, head_dim, hip_stream);
+}
+
+static int dense_common(const void* q, const void* k, const void* v, int64_t batch,
+                        int64_t num_heads, int64_t num_kv_heads, int64_t seqlen_q,
+                        int64_t kv_capacity, int64_t head_dim, int causal, int64_t window_size,
+                        int64_t kv_seq_len, int elem, double score_mul, double out_mul,
+                        void* out, float* lse, void* hip_stream) {
+  int rc;
+  if ((rc = check_head_dim(head_dim))) return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads))) return rc;
+  if (batch < 0) return fail(VLGQA_EINVAL, "batch", "must be non-negative");
+  if (seqlen_q < 0) return fail(VLGQA_EINVAL, "seqlen_q", "must be non-negative");
+  if (kv_capacity < 0) return fail(VLGQA_EINVAL, "kv_capacity", "must be non-negative");
+  if (window_size < 0) return fail(VLGQA_EINVAL, "window_size", "must be non-negative");
+  if (causal != 0 && causal != 1) return fail(VLGQA_EINVAL, "causal", "must be 0 or 1");
+  const int64_t n = kv_seq_len < 0 ? kv_capacity : kv_seq_len;
+  if (n > kv_capacity) return fail(VLGQA_EINVAL, "kv_seq_len", "exceeds the K/V buffer capacity");
+  if (seqlen_q > INT32_MAX || kv_capacity > INT32_MAX || batch > INT32_MAX)
+    return fail(VLGQA_EINVAL, "seqlen_q", "extents must fit 32 bits");
+  if (window_size > INT32_MAX) window_size = INT32_MAX;
+  if (batch == 0 || seqlen_q == 0) return VLGQA_OK;
+  if ((rc = check_ptr(q, "q"))) return rc;
+  if (n > 0) {
+    if ((rc = check_ptr(k, "k"))) return rc;
+    if ((rc = check_ptr(v, "v"))) return rc;
+  }
+  if ((rc = check_ptr(out, "out"))) return rc;
+  if ((rc = check_ptr(lse, "lse"))) return rc;
+
+  vlgqa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
+  p.cu_q = nullptr; p.cu_k = nullptr;
+  p.q_bs = num_heads * seqlen_q * head_dim; p.q_rs = head_dim; p.q_hs = seqlen_q * head_dim;
+  p.k_bs = num_kv_heads * kv_capacity * head_dim; p.k_rs = head_dim; p.k_hs = kv_capacity * head_dim;
+  p.o_bs = p.q_bs; p.o_rs = p.q_rs; p.o_hs = p.q_hs;
+  p.l_bs = num_heads * seqlen_q; p.l_rs = 1; p.l_hs = seqlen_q;
+  p.batch = (int32_t)batch;
+  p.heads = (int32_t)num_heads;
+  p.kv_heads = (int32_t)num_kv_heads;
+  p.group = (int32_t)(num_heads / num_kv_heads);
+  p.seqlen_q = (int32_t)seqlen_q;
+  p.seqlen_k = (int32_t)n;
+  p.causal = causal;
+  p.window = (int32_t)window_size;
+  p.score_mul = (float)score_mul;
+  p.out_mul = (float)out_mul;
+  return finish_and_launch(p, seqlen_q, elem, head_dim, hip_stream);
+}
+
+int flash_attention_fwd(const void* q, const void* k, const void* v, int64_t batch,
+                        int64_t num_heads, int64_t num_kv_heads, int64_t seqlen_q,
+                        int64_t kv_capacity, int64_t head_dim, int causal, int64_t window_size,
+                        int64_t kv_seq_len, int dtype, void* out, float* lse, void* hip_stream) {
+  g_last_error.clear();
+  int rc, elem = 0;
+  if ((rc = elem_of_dtype(dtype, &elem))) return rc;
+  const double mul = 1.4426950408889634 / std::sqrt((double)(head_dim > 0 ? head_dim : 1));
+  return dense_common(q, k, v, batch, num_heads, num_kv_heads, seqlen_q, kv_capacity, head_dim,
+                      causal, window_size, kv_seq_len, elem, mul, 1.0, out, lse, hip_stream);
+}
+
+int flash_attention_fwd_fp8(const void* q, const void* k, const void* v, int64_t batch,
+                            int64_t num_heads, int64_t num_kv_heads, int64_t seqlen_q,
+                            int64_t seqlen_k, int64_t head_dim, int causal, float q_scale,
+                            float k_scale, float v_scale, float o_scale, void* out, float* lse,
+                            void* hip_stream) {
+  g_last_error.clear();
+  const struct { const char* name; float value; } scales[] = {
+      {"q_scale", q_scale}, {"k_scale", k_scale}, {"v_scale", v_scale}, {"o_scale", o_scale}};
+  for (const auto& s : scales)
+    if (!std::isfinite(s.value) || !(s.value > 0.0f))
+      return fail(VLGQA_EINVAL, s.name, "must be finite and positive");
+  const double mul = (double)q_scale * (double)k_scale * 1.4426950408889634 /
+                     std::sqrt((double)(head_dim > 0 ? head_dim : 1));
+  const double omul = (double)v_scale / (double)o_scale;
+  if (!std::isfinite(mul) || !std::isfinite(omul) || mul == 0.0 || omul == 0.0 ||
+      (float)mul == 0.0f || std::isinf((float)mul) || std::isinf((float)omul))
+    return fail(VLGQA_EINVAL, "q_scale", "scale products overflow or underflow f32");
+  return dense_common(q, k, v, batch, num_heads, num_kv_heads, seqlen_q, seqlen_k, head_dim,
+                      causal, 0, -1, vlgqa::E_E4M3, mul, omul, out, lse, hip_stream);
+}
+
+}  // extern "C"

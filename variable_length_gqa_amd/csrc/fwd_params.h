@@ -1,0 +1,47 @@
+// Launch parameters shared by the C ABI (host) and the forward kernels.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace vlgqa {
+
+// storage element kinds of q/k/v/out
+enum Elem : int { E_F32 = 0, E_F16 = 1, E_BF16 = 2, E_E4M3 = 3 };
+
+// query rows per workgroup (4 waves x 32 rows) and keys per K/V tile
+constexpr int kBlockM = 128;
+constexpr int kBlockN = 64;
+constexpr int kThreads = 256;
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  // packed layout: sequence b spans rows cu[b] .. cu[b+1]; null for dense
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  // strides in elements: batch, row (token), head
+  int64_t q_bs, q_rs, q_hs;
+  int64_t k_bs, k_rs, k_hs;  // shared by v
+  int64_t o_bs, o_rs, o_hs;
+  int64_t l_bs, l_rs, l_hs;
+  int32_t batch, heads, kv_heads, group;
+  int32_t seqlen_q, seqlen_k;  // dense extents (per-sequence lengths come from cu_* when given)
+  int32_t causal, window;
+  int32_t n_qtiles;  // ceil(max_seqlen_q / kBlockM)
+  int32_t n_groups;  // n_qtiles * batch * kv_heads
+  float score_mul;   // multiplies q.k into the log2 domain: scale * log2(e) [* q_scale * k_scale]
+  float out_mul;     // multiplies the normalised output: 1, or v_scale / o_scale for E4M3
+};
+
+// Number of workgroups the forward launch uses for these parameters.
+inline int64_t fwd_grid_size(const FwdParams& p) {
+  int64_t groups8 = ((int64_t)p.n_groups + 7) / 8 * 8;
+  return groups8 * p.group;
+}
+
+hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t stream);
+
+}  // namespace vlgqa
