@@ -148,7 +148,7 @@ def cpu_baseline(name, x, n_heads, unit_scale):
                                        x.kv_seq_len, workers=workers, heads=heads)
         fl = F.attention_flops([Sq] * B, [n] * B, n_heads, D, x.causal, x.window)
     secs = time.perf_counter() - t0
-    return {"value": fl / secs / unit_scale, "unit": "TFLOP/s", "cores": workers,
+    return secs, {"value": fl / secs / unit_scale, "unit": "TFLOP/s", "cores": workers,
             "kind": "oracle",
             "sample": f"query heads 0..{n_heads - 1} of {x.num_heads} of every sequence "
                       f"({fl:.3e} algorithmic FLOPs, {secs:.1f} s wall, f64 NumPy, "
@@ -162,7 +162,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="varlen_bf16_long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="query heads in the CPU-baseline sample (0: sized to ~15 s)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward shards across GPUs by heads or by "
@@ -177,6 +180,16 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
+                          "launches": max(1, args.steps)}), flush=True)
+        return
     x, step, flops, io, cfg, dt = make_step(args.workload, dev)
 
     for _ in range(args.warmup):
@@ -210,8 +223,14 @@ def main():
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.workload, x, min(args.cpu_heads, x.num_heads),
-                                           1e12)
+        n_heads = args.cpu_heads
+        if n_heads <= 0:
+            # size the sample to about 15 s: time one head group, then scale up
+            G = x.num_heads // x.num_kv_heads
+            secs, _ = cpu_baseline(args.workload, x, min(G, x.num_heads), 1e12)
+            n_heads = int(min(x.num_heads, max(G, G * round(15.0 / max(secs, 1e-3)))))
+        _, res["cpu_baseline"] = cpu_baseline(args.workload, x, min(n_heads, x.num_heads),
+                                              1e12)
     print(json.dumps(res), flush=True)
 
 
