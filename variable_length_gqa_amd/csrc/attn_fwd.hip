@@ -327,7 +327,9 @@ __device__ __forceinline__ void load_tile16(const FwdParams& p, const Work& w, i
     st.k[c] = z;
   }
   if (tid < T::V_UNITS) {
-    const int db = tid % (D / 8), kq = tid / (D / 8);
+    // key quad fastest across lanes: the transposed LDS writes of 16 lanes then
+    // fill 16 different 8-byte slots of one V^T row (no bank conflicts)
+    const int kq = tid % (kBlockN / 4), db = tid / (kBlockN / 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = c0 + 4 * kq + j;
@@ -365,7 +367,7 @@ __device__ __forceinline__ void store_tile16(uint16_t* sK, uint16_t* sV, int tid
     }
   }
   if (tid < T::V_UNITS) {
-    const int db = tid % (D / 8), kq = tid / (D / 8);
+    const int kq = tid % (kBlockN / 4), db = tid / (kBlockN / 4);
     // rows j = 0..3 (keys 4kq + j) as 8 x 16-bit each: w[j][i] holds d = 2i, 2i+1
     uint32_t w[4][4];
 #pragma unroll
