@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fwd_params.h"
 
 namespace vlgqa {
@@ -76,15 +78,17 @@ __device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
-// two floats -> packed 16-bit pair (round to nearest even)
+// two floats -> packed 16-bit pair (round to nearest even), one v_cvt_pk_*
 template <int ELEM>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
   if constexpr (ELEM == E_F16) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   } else {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
 }
 
@@ -130,30 +134,31 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 // ---------------------------------------------------------------------------
 //
 // Workgroups are handed to the 8 XCDs round-robin (block i -> XCD i % 8).  A
-// "group" is (query tile, sequence, kv head); its G query heads read the same
-// K/V, so they are placed on consecutive slots of ONE XCD and share its L2.
-// Groups are ordered by descending query tile: under a causal mask later
-// tiles see more keys, so the longest work is dispatched first.
+// "group" is (query tile, sequence, kv head); the workgroups of a group cover
+// its G query heads (heads_per_wg at a time) and read the same K/V, so they
+// are placed on consecutive slots of ONE XCD and share its L2.  Groups are
+// ordered by descending query tile: under a causal mask later tiles see more
+// keys, so the longest work is dispatched first.
 struct Work {
-  int b, h, kvh, r0;
+  int b, kvh, h0, r0;
   int q_start, Lq, k_start, Lk;
 };
 
 __device__ __forceinline__ bool decode_work(const FwdParams& p, Work& w) {
-  const int G = p.group;
+  const int G2 = p.group / p.heads_per_wg;  // workgroups per group
   const int pid = blockIdx.x;
   const int xcd = pid & 7;
   const int slot = pid >> 3;
-  const int gq = slot / G;
-  const int g = slot - gq * G;
+  const int gq = slot / G2;
+  const int g2 = slot - gq * G2;
   const int grp = gq * 8 + xcd;
   if (grp >= p.n_groups) return false;
   w.kvh = grp % p.kv_heads;
   const int t2 = grp / p.kv_heads;
   w.b = t2 % p.batch;
   const int tidx = t2 / p.batch;
-  w.r0 = (p.n_qtiles - 1 - tidx) * kBlockM;
-  w.h = w.kvh * G + g;
+  w.r0 = (p.n_qtiles - 1 - tidx) * p.rows_per_wg;
+  w.h0 = w.kvh * p.group + g2 * p.heads_per_wg;
   w.q_start = 0;
   w.Lq = p.seqlen_q;
   w.k_start = 0;
@@ -169,16 +174,34 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, Work& w) {
   return w.r0 < w.Lq;
 }
 
-// ---------------------------------------------------------------------------
-// per-lane online-softmax state and the shared pieces of the tile loop
-// ---------------------------------------------------------------------------
+// Key range [lo, hi) visible to query rows [qa, qb] of a sequence.
+__device__ __forceinline__ void key_range(const FwdParams& p, const Work& w, int qa, int qb,
+                                          int& lo, int& hi) {
+  const int off = w.Lk - w.Lq;
+  const bool upper = p.causal || p.window > 0;
+  hi = upper ? min(w.Lk, qb + off + 1) : w.Lk;
+  lo = p.window > 0 ? max(0, qa + off - p.window + 1) : 0;
+}
 
-template <int NOB>
-struct RowState {
-  float m;         // reference maximum, log2 domain (score * score_mul)
-  float l;         // this lane's half of the running denominator
-  f32x16 o[NOB];   // O^T accumulators: query (lane % 32), 16 d values per block
-};
+// Range-checked loads: a buffer resource covering [base, base + bytes) returns
+// zeros for any access at or beyond `bytes` (rows past a sequence's end).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t sat_bytes(int64_t b) {
+  return b > 0xFFFFFFFFll ? 0xFFFFFFFFu : (b < 0 ? 0u : (uint32_t)b);
+}
+
+// ---------------------------------------------------------------------------
+// shared softmax / epilogue pieces
+// ---------------------------------------------------------------------------
 
 // Mask the S^T accumulators of a 64-key tile starting at key c0 for the
 // lane's query row q.  Key of register r in block kb: c0 + 32 kb + 8 (r / 4)
@@ -197,66 +220,53 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int c0, int hl, int q,
   }
 }
 
-// One online-softmax step over the 64 scores of this lane's row (2 blocks x 16
-// registers, the other 32 scores of the row live in lane ^ 32).  Leaves the
-// probabilities (relative to the reference maximum) in s.  EXACT rounds
-// score * mul before subtracting the reference, so the maximal score maps to
-// exactly exp2(0) = 1 (one more VALU op per score; used by the f32 kernel).
-template <int NOB, bool EXACT = false>
-__device__ __forceinline__ void softmax_step(f32x16 (&s)[2], RowState<NOB>& st, float mul) {
-  float mx = s[0][0];
+// max over the 64 scores of the lane's row in one tile (32 here, 32 in lane ^ 32)
+__device__ __forceinline__ float tile_row_max(const f32x16 (&s)[2]) {
+  float a = fmaxf(s[0][0], s[1][0]), b = fmaxf(s[0][1], s[1][1]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-  mx = swap_halves_max(mx) * mul;  // -inf stays -inf
-  const bool up = mx > st.m + kRescaleSlack;  // st.m = -inf: any finite maximum moves it
-  if (wave_any(up)) {
-    const float alpha = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.0f;
-    st.m = up ? mx : st.m;
-    st.l *= alpha;
-#pragma unroll
-    for (int i = 0; i < NOB; ++i) st.o[i] *= alpha;
+  for (int r = 2; r < 16; r += 2) {
+    a = fmaxf(a, fmaxf(s[0][r], s[1][r]));
+    b = fmaxf(b, fmaxf(s[0][r + 1], s[1][r + 1]));
   }
-  const float ref = st.m == -INFINITY ? 0.0f : st.m;
-  float sum = 0.0f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float arg;
-      if constexpr (EXACT) {
-#pragma clang fp contract(off)
-        const float t = s[kb][r] * mul;  // rounded on its own, not fused into the subtraction
-        arg = t - ref;
-      } else {
-        arg = __builtin_fmaf(s[kb][r], mul, -ref);
-      }
-      const float pr = __builtin_amdgcn_exp2f(arg);
-      s[kb][r] = pr;
-      sum += pr;
-    }
-  }
-  st.l += sum;
+  return swap_halves_max(fmaxf(a, b));
 }
 
-// Normalise and store O (rows of the lane's query, 4 consecutive d per store)
-// and LSE.  OUT_ELEM selects the storage conversion.
+// Move the reference maximum m of a row to mx (log2 domain) when the tile
+// raises it by more than kRescaleSlack; rescale l and o to match.  The caller
+// has the wave-uniform "any lane moves" test around it.
+template <int NOB>
+__device__ __forceinline__ void rescale_row(float mx, float& m, float& l, f32x16 (&o)[NOB]) {
+  const bool up = mx > m + kRescaleSlack;
+  const float alpha = up ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;
+  m = up ? mx : m;
+  l *= alpha;
+#pragma unroll
+  for (int i = 0; i < NOB; ++i) o[i] *= alpha;
+}
+
+template <int NOB>
+struct RowState {
+  float m;         // reference maximum, log2 domain (score * score_mul)
+  float l;         // this lane's half of the running denominator
+  f32x16 o[NOB];   // O^T accumulators: query (lane % 32), 16 d values per block
+};
+
+// Normalise and store one query row's O (4 consecutive d per store) and LSE.
 template <int OUT_ELEM, int D>
-__device__ __forceinline__ void store_rows(const FwdParams& p, const Work& w, int qrow, int hl,
-                                           RowState<D / 32>& st) {
-  const float ltot = swap_halves_sum(st.l);
+__device__ __forceinline__ void store_row(const FwdParams& p, const Work& w, int h, int qrow,
+                                          int hl, float m, float l, const f32x16 (&o)[D / 32]) {
+  const float ltot = swap_halves_sum(l);
   if (qrow >= w.Lq) return;
   const float inv = ltot > 0.0f ? p.out_mul / ltot : 0.0f;
   const int64_t orow = (int64_t)w.b * p.o_bs + (int64_t)(w.q_start + qrow) * p.o_rs +
-                       (int64_t)w.h * p.o_hs;
+                       (int64_t)h * p.o_hs;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = db * 32 + g * 8 + 4 * hl;
-      const float x0 = st.o[db][4 * g + 0] * inv, x1 = st.o[db][4 * g + 1] * inv;
-      const float x2 = st.o[db][4 * g + 2] * inv, x3 = st.o[db][4 * g + 3] * inv;
+      const float x0 = o[db][4 * g + 0] * inv, x1 = o[db][4 * g + 1] * inv;
+      const float x2 = o[db][4 * g + 2] * inv, x3 = o[db][4 * g + 3] * inv;
       if constexpr (OUT_ELEM == E_F32) {
         f32x4 v = {x0, x1, x2, x3};
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d0) = v;
@@ -271,26 +281,326 @@ __device__ __forceinline__ void store_rows(const FwdParams& p, const Work& w, in
     }
   }
   if (hl == 0) {
-    const float lse = ltot > 0.0f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -INFINITY;
-    p.lse[(int64_t)w.b * p.l_bs + (int64_t)(w.q_start + qrow) * p.l_rs + (int64_t)w.h * p.l_hs] = lse;
+    const float lse = ltot > 0.0f ? (m + __builtin_log2f(ltot)) * kLn2 : -INFINITY;
+    p.lse[(int64_t)w.b * p.l_bs + (int64_t)(w.q_start + qrow) * p.l_rs + (int64_t)h * p.l_hs] = lse;
   }
 }
 
-// Key range [lo, hi) visible to query rows [qa, qb] of a sequence.
-__device__ __forceinline__ void key_range(const FwdParams& p, const Work& w, int qa, int qb,
-                                          int& lo, int& hi) {
+struct KvSrc {
+  __amdgpu_buffer_rsrc_t k, v;  // this (sequence, kv head)'s K/V, range = its Lk rows
+  uint32_t rs;                  // row stride in bytes
+};
+
+// ---------------------------------------------------------------------------
+// bf16 / f16 kernel
+// ---------------------------------------------------------------------------
+//
+// One workgroup = 128 query rows of one head, 4 waves x 32 rows; two
+// workgroups share a CU, so the two waves on a SIMD belong to independent
+// workgroups and one's vector work (softmax) overlaps the other's matrix work.
+// Per 64-key tile a wave does 16 MFMAs for S^T = K Q^T, the softmax of its
+// 32 x 64 scores, and 16 MFMAs for O^T += V^T P^T.
+//
+// K and V tiles reach LDS by DMA (buffer loads that write LDS directly: no
+// staging registers, no vector instructions), double-buffered: the next tile
+// is requested at the start of a tile and awaited at its end, and one
+// workgroup barrier per tile publishes it.  That barrier orders LDS only, so
+// it does not drain other requests.  The DMA is written out as plain
+// instructions the compiler does not track; it would otherwise stall every
+// transposing V read on it, since it cannot tell the V buffers apart.
+// Ordering is by the explicit vmcnt wait before each barrier.  V is stored
+// row-major and read as the V^T operand with the transposing
+// ds_read_b64_tr_b16.  Rows are stored unpadded with their 16-byte chunks
+// XOR-swizzled by the row index, which keeps both read patterns free of bank
+// conflicts: K fragments (16 rows x one chunk per 16 lanes) and V^T fragments
+// (4 rows x 4 chunks per 32 lanes of a transposing read).  All LDS read
+// addresses are computed once; tile-to-tile they differ by immediate offsets.
+// The buffer range of a (sequence, kv head) ends at its last key, so rows past
+// it arrive as zeros.
+
+template <int ELEM, int D>
+struct Cfg5 {
+  static constexpr int NS = D / 16;                  // MFMA k-steps over d
+  static constexpr int NOB = D / 32;                 // O^T accumulator blocks
+  static constexpr int ROWB = D * 2;                 // bytes per K/V row in LDS
+  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  static constexpr int TILE = kBlockN * ROWB;        // bytes of one K (or V) tile
+  static constexpr int CPT = TILE / 16 / kThreads;   // DMA chunks per thread per tensor
+  static_assert(CPT >= 1 && (TILE / 16) % kThreads == 0, "tile shape");
+};
+
+// chunk swizzle of an LDS row: physical chunk = logical chunk ^ swz(row)
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);  // 16 chunks per row
+  else return (row >> 1) & 7;                                       // 8 chunks per row
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
+// (lgkmcnt) but lets global loads and LDS DMA stay in flight across it.  A
+// __syncthreads(), and even an LDS-scoped fence, drains every outstanding
+// vector-memory request (DMA writes count as LDS stores).  DMA into LDS is
+// published by an explicit vmcnt wait before this.  The empty asm statements
+// with a memory clobber keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// wait until no vector-memory request of this wave is outstanding
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Raw buffer descriptor words (base, stride 0, byte range, gfx9 flags).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r = {(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+  return r;
+}
+
+// Request one tile (rows c0 .. c0+63) of K or V into an LDS tile buffer: this
+// thread's chunk n goes to LDS chunk (wid*CPT + n)*64 + lane, from tile offset
+// voff[n].  The instruction writes LDS only (no register results).
+template <int ELEM, int D>
+__device__ __forceinline__ void dma_tile(uint8_t* buf, u32x4 rsrc, uint32_t base, int wid,
+                                         const uint32_t (&voff)[Cfg5<ELEM, D>::CPT]) {
+  using C = Cfg5<ELEM, D>;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)buf;
+#pragma unroll
+  for (int n = 0; n < C::CPT; ++n) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (wid * C::CPT + n) * 1024);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(dst), "v"(base + voff[n]), "s"(rsrc)
+        : "memory", "m0");
+  }
+}
+
+// one V^T operand (32 d x 16 keys) by two transposing reads
+__device__ __forceinline__ u32x4 vt_operand(const uint8_t* p0, const uint8_t* p1) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+template <int ELEM, int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void fwd16_kernel(FwdParams p) {
+  using C = Cfg5<ELEM, D>;
+  constexpr int OUT = ELEM;
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv1[C::TILE];
+
+  Work w;
+  if (!decode_work(p, w)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ql = lane & 31;
+  const int h = w.h0;
+  const int qrow = w.r0 + 32 * wid + ql;  // this lane's query row within the sequence
+  const float mul = p.score_mul;
+
+  // Q^T fragments: lane holds q[qrow][16 ks + 8 hl .. +8]; only ever an MFMA
+  // operand, so it is parked in AGPRs (MFMA reads them directly)
+  u32x4 qf[C::NS];
+  {
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(p.q) +
+                           ((int64_t)w.b * p.q_bs + (int64_t)w.q_start * p.q_rs +
+                            (int64_t)h * p.q_hs) * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qbase, sat_bytes((int64_t)w.Lq * p.q_rs * 2));
+    const uint32_t roff = (uint32_t)qrow * (uint32_t)(p.q_rs * 2);
+#pragma unroll
+    for (int ks = 0; ks < C::NS; ++ks) qf[ks] = bload16(qr, roff + (16 * ks + 8 * hl) * 2);
+#pragma unroll
+    for (int ks = 0; ks < C::NS; ++ks) asm volatile("" : "=a"(qf[ks]) : "0"(qf[ks]));
+  }
+
+  // K/V of this (sequence, kv head): descriptors and per-thread tile offsets
+  u32x4 krs, vrs;
+  uint32_t rs;
+  {
+    const int64_t koff = ((int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs +
+                          (int64_t)w.kvh * p.k_hs) * 2;
+    const uint32_t bytes = sat_bytes((int64_t)w.Lk * p.k_rs * 2);
+    krs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
+    vrs = rsrc_words(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
+    rs = (uint32_t)(p.k_rs * 2);
+  }
+  uint32_t voff[C::CPT];
+#pragma unroll
+  for (int n = 0; n < C::CPT; ++n) {
+    const int P = (wid * C::CPT + n) * 64 + lane;
+    const int row = P / C::CPR, ch = (P % C::CPR) ^ swz<D>(row);
+    voff[n] = (uint32_t)row * rs + ch * 16;
+  }
+  // LDS read offsets (tile-relative), fixed for the whole loop:
+  //  K fragment (kb, ks): row 32 kb + ql, logical chunk 2 ks + hl  (kb via +32 rows)
+  //  (offset of step ks = koff0 ^ (ks << 5): the swizzled chunk index 2 ks + hl
+  //  XOR swz(ql) differs from step 0's in chunk bits 1.. only)
+  const uint32_t koff0 = (uint32_t)ql * C::ROWB + (uint32_t)((hl ^ swz<D>(ql)) * 16);
+  //  V^T operand (t2, db), transposing read c: this lane supplies row
+  //  16 t2 + 8 c + 4 (g / 2) + e, d = 32 db + 16 (g % 2) + 4 j, where g is the
+  //  16-lane group, e = (lane % 16) / 4, j = lane % 4  (t2 via +16 rows)
+  uint32_t voffs[C::NOB][2];
+  {
+    const int g = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
+#pragma unroll
+    for (int db = 0; db < C::NOB; ++db)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = 8 * c + 4 * (g >> 1) + e;
+        const int ch = 4 * db + 2 * (g & 1) + (j >> 1);
+        voffs[db][c] = (uint32_t)row * C::ROWB + (uint32_t)((ch ^ swz<D>(row)) * 16) + (j & 1) * 8;
+      }
+  }
+
   const int off = w.Lk - w.Lq;
   const bool upper = p.causal || p.window > 0;
-  hi = upper ? min(w.Lk, qb + off + 1) : w.Lk;
-  lo = p.window > 0 ? max(0, qa + off - p.window + 1) : 0;
+  int kv_lo, kv_hi;
+  key_range(p, w, w.r0, min(w.r0 + p.rows_per_wg, w.Lq) - 1, kv_lo, kv_hi);
+  const int t0 = kv_lo / kBlockN;
+  const int t1 = kv_hi > kv_lo ? (kv_hi + kBlockN - 1) / kBlockN : t0;
+  const int wa = w.r0 + 32 * wid, wb = min(wa + 31, w.Lq - 1);
+  int wlo = 0, whi = 0;
+  if (wa <= wb) key_range(p, w, wa, wb, wlo, whi);
+
+  RowState<C::NOB> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int i = 0; i < C::NOB; ++i) st.o[i] = f32x16{};
+
+  if (t0 < t1) {
+    dma_tile<ELEM, D>(lk0, krs, (uint32_t)(t0 * kBlockN) * rs, wid, voff);
+    dma_tile<ELEM, D>(lv0, vrs, (uint32_t)(t0 * kBlockN) * rs, wid, voff);
+  }
+  wait_vm_all();
+  lds_barrier();
+
+  auto tile = [&](int t, const uint8_t* kb_, const uint8_t* vb_, uint8_t* knext,
+                  uint8_t* vnext) __attribute__((always_inline)) {
+    if (t + 1 < t1) {
+      const uint32_t base = (uint32_t)((t + 1) * kBlockN) * rs;
+      dma_tile<ELEM, D>(knext, krs, base, wid, voff);
+      dma_tile<ELEM, D>(vnext, vrs, base, wid, voff);
+    }
+    const int c0 = t * kBlockN;
+    if (wa <= wb && c0 < whi && c0 + kBlockN > wlo) {
+      // S^T = K Q^T for the two 32-key blocks
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int ks = 0; ks < C::NS; ++ks) {
+        const uint32_t ko = koff0 ^ (uint32_t)(ks << 5);
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kb_ + ko);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kb_ + ko + 32 * C::ROWB);
+        s[0] = mfma16<ELEM>(a0, qf[ks], s[0]);
+        s[1] = mfma16<ELEM>(a1, qf[ks], s[1]);
+      }
+      const bool need_mask = (c0 + kBlockN > w.Lk) || (upper && c0 + kBlockN - 1 > wa + off) ||
+                             (p.window > 0 && c0 < wb + off - p.window + 1);
+      if (need_mask) mask_tile(s, c0, hl, qrow, off, w.Lk, upper, p.window);
+
+      // online softmax over the row's 64 scores (32 here, 32 in lane ^ 32)
+      float mx;
+      {
+        float a = __builtin_elementwise_maximum(s[0][0], s[1][0]);
+        float b = __builtin_elementwise_maximum(s[0][1], s[1][1]);
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) {
+          a = __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(s[0][r], s[1][r]));
+          b = __builtin_elementwise_maximum(b, __builtin_elementwise_maximum(s[0][r + 1], s[1][r + 1]));
+        }
+        mx = swap_halves_max(__builtin_elementwise_maximum(a, b)) * mul;
+      }
+      if (wave_any(mx > st.m + kRescaleSlack)) rescale_row<C::NOB>(mx, st.m, st.l, st.o);
+      const float ref = st.m == -INFINITY ? 0.0f : st.m;
+      u32x4 pk[4];
+      float sum0 = 0.0f, sum1 = 0.0f;
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const f32x16& sb = s[t2 >> 1];
+        const int r = 8 * (t2 & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r + 2 * i], mul, -ref));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r + 2 * i + 1], mul, -ref));
+          sum0 += p0;
+          sum1 += p1;
+          pk[t2][i] = pack2<ELEM>(p0, p1);
+        }
+      }
+      st.l += sum0 + sum1;
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) {
+#pragma unroll
+        for (int db = 0; db < C::NOB; ++db) {
+          const u32x4 a = vt_operand(vb_ + voffs[db][0] + t2 * 16 * C::ROWB,
+                                     vb_ + voffs[db][1] + t2 * 16 * C::ROWB);
+          st.o[db] = mfma16<ELEM>(a, pk[t2], st.o[db]);
+        }
+      }
+    }
+    wait_vm_all();  // tile t+1 has landed (this wave's part)
+    lds_barrier();  // ... and everyone's
+  };
+
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
+    tile(t, lk0, lv0, lk1, lv1);
+    tile(t + 1, lk1, lv1, lk0, lv0);
+  }
+  if (t < t1) tile(t, lk0, lv0, lk1, lv1);
+
+  store_row<OUT, D>(p, w, h, qrow, hl, st.m, st.l, st.o);
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit compute kernel (bf16, f16, and E4M3 widened to bf16 on the way in)
+// E4M3 kernel: codes widened to bf16 on the way into LDS, 32 rows per wave
 // ---------------------------------------------------------------------------
+//
+// One workgroup = 128 query rows of one head, 4 waves x 32 rows, two
+// workgroups per CU.  K/V tiles of 64 keys go global -> registers (one tile
+// ahead) -> LDS (double buffered): K row-major, V transposed (a 4x8 register
+// transpose) with the middle two 4-key quads of every 16 keys swapped to match
+// the order of the P operand.  E4M3 values are exact in bf16, so the widening
+// loses nothing; the per-tensor scales are folded into the score multiplier
+// and the output multiplier.
+
+template <int NOB>
+__device__ __forceinline__ void softmax_step8(f32x16 (&s)[2], RowState<NOB>& st, float mul) {
+  const float mx = tile_row_max(s) * mul;  // -inf stays -inf
+  if (wave_any(mx > st.m + kRescaleSlack)) rescale_row<NOB>(mx, st.m, st.l, st.o);
+  const float ref = st.m == -INFINITY ? 0.0f : st.m;
+  float sum = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], mul, -ref));
+      s[kb][r] = pr;
+      sum += pr;
+    }
+  }
+  st.l += sum;
+}
 
 template <int ELEM, int D>
-struct Tile16 {
+struct Tile8 {
   static constexpr int KP = D + 8;          // K row pitch in LDS (u16), 16 B pad
   static constexpr int VP = kBlockN + 8;    // V^T row pitch in LDS (u16)
   static constexpr int EB = ELEM == E_E4M3 ? 1 : 2;  // stored bytes per element
@@ -303,15 +613,15 @@ struct Tile16 {
 };
 
 template <int ELEM, int D>
-struct Staging16 {
-  u32x4 k[Tile16<ELEM, D>::K_CPT];
+struct Staging8 {
+  u32x4 k[Tile8<ELEM, D>::K_CPT];
   u32x4 v[4];  // 4 key rows x 8 d (E4M3: only the low 2 words used)
 };
 
 template <int ELEM, int D>
-__device__ __forceinline__ void load_tile16(const FwdParams& p, const Work& w, int c0, int tid,
-                                            Staging16<ELEM, D>& st) {
-  using T = Tile16<ELEM, D>;
+__device__ __forceinline__ void load_tile8(const FwdParams& p, const Work& w, int c0, int tid,
+                                            Staging8<ELEM, D>& st) {
+  using T = Tile8<ELEM, D>;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) +
                          ((int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs + (int64_t)w.kvh * p.k_hs) * T::EB;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) +
@@ -349,9 +659,9 @@ __device__ __forceinline__ void load_tile16(const FwdParams& p, const Work& w, i
 }
 
 template <int ELEM, int D>
-__device__ __forceinline__ void store_tile16(uint16_t* sK, uint16_t* sV, int tid,
-                                             const Staging16<ELEM, D>& st) {
-  using T = Tile16<ELEM, D>;
+__device__ __forceinline__ void store_tile8(uint16_t* sK, uint16_t* sV, int tid,
+                                             const Staging8<ELEM, D>& st) {
+  using T = Tile8<ELEM, D>;
 #pragma unroll
   for (int c = 0; c < T::K_CPT; ++c) {
     const int idx = c * kThreads + tid;
@@ -399,8 +709,8 @@ __device__ __forceinline__ void store_tile16(uint16_t* sK, uint16_t* sV, int tid
 
 template <int ELEM, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
-void fwd16_kernel(FwdParams p) {
-  using T = Tile16<ELEM, D>;
+void fwd8_kernel(FwdParams p) {
+  using T = Tile8<ELEM, D>;
   constexpr int NS = D / 16;   // MFMA k-steps over d
   constexpr int NOB = D / 32;  // O^T accumulator blocks
   constexpr int OUT = ELEM;    // output stored in the input format
@@ -411,7 +721,7 @@ void fwd16_kernel(FwdParams p) {
   Work w;
   if (!decode_work(p, w)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
   const int qrow = w.r0 + wid * 32 + ql;  // this lane's query row within the sequence
 
@@ -420,7 +730,7 @@ void fwd16_kernel(FwdParams p) {
   {
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(p.q) +
                         ((int64_t)w.b * p.q_bs + (int64_t)(w.q_start + qrow) * p.q_rs +
-                         (int64_t)w.h * p.q_hs) * T::EB;
+                         (int64_t)w.h0 * p.q_hs) * T::EB;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       u32x4 z = {0u, 0u, 0u, 0u};
@@ -443,7 +753,7 @@ void fwd16_kernel(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < NOB; ++i) st.o[i] = f32x16{};
 
-  const int rlast = min(w.r0 + kBlockM, w.Lq) - 1;
+  const int rlast = min(w.r0 + p.rows_per_wg, w.Lq) - 1;
   int kv_lo, kv_hi;
   key_range(p, w, w.r0, rlast, kv_lo, kv_hi);
   // this wave's rows and keys
@@ -457,16 +767,16 @@ void fwd16_kernel(FwdParams p) {
   const int t0 = kv_lo / kBlockN;
   const int t1 = kv_hi > kv_lo ? (kv_hi + kBlockN - 1) / kBlockN : t0;
 
-  Staging16<ELEM, D> stg;
-  if (t0 < t1) load_tile16<ELEM, D>(p, w, t0 * kBlockN, tid, stg);
+  Staging8<ELEM, D> stg;
+  if (t0 < t1) load_tile8<ELEM, D>(p, w, t0 * kBlockN, tid, stg);
 
   for (int t = t0; t < t1; ++t) {
     const int buf = (t - t0) & 1;
     uint16_t* k_s = sK[buf];
     uint16_t* v_s = sV[buf];
-    store_tile16<ELEM, D>(k_s, v_s, tid, stg);
+    store_tile8<ELEM, D>(k_s, v_s, tid, stg);
     __syncthreads();
-    if (t + 1 < t1) load_tile16<ELEM, D>(p, w, (t + 1) * kBlockN, tid, stg);
+    if (t + 1 < t1) load_tile8<ELEM, D>(p, w, (t + 1) * kBlockN, tid, stg);
 
     const int c0 = t * kBlockN;
     if (!wave_live || c0 >= whi || c0 + kBlockN <= wlo) continue;
@@ -485,7 +795,7 @@ void fwd16_kernel(FwdParams p) {
                            (p.window > 0 && c0 < wb + off - p.window + 1);
     if (need_mask) mask_tile(s, c0, hl, qrow, off, w.Lk, upper, p.window);
 
-    softmax_step<NOB>(s, st, p.score_mul);
+    softmax_step8<NOB>(s, st, p.score_mul);
 
     // P^T operands: step t2 uses registers 8 (t2 % 2) .. +7 of block t2 / 2
     u32x4 pk[4];
@@ -507,18 +817,47 @@ void fwd16_kernel(FwdParams p) {
     }
   }
 
-  store_rows<OUT, D>(p, w, qrow, hl, st);
+  store_row<OUT, D>(p, w, w.h0, qrow, hl, st.m, st.l, st.o);
 }
+
 
 // ---------------------------------------------------------------------------
 // f32 kernel (v_mfma_f32_32x32x2_f32: exact products, f32 accumulation)
 // ---------------------------------------------------------------------------
 //
-// The d contraction order is permuted consistently for Q and K: MFMA step s,
-// lane half h <-> d = (D/2) h + s, so each lane reads contiguous d values.
-// P.V: step r of key block kb pairs the keys 32 kb + 8 (r/4) + 4 h + r%4
-// (h = lane half), which is exactly what accumulator register r holds, so P
-// needs no movement and V stays row-major in LDS.
+// 4 waves x 32 query rows of one head per workgroup.  The d contraction order
+// is permuted consistently for Q and K: MFMA step s, lane half h <-> d =
+// (D/2) h + s, so each lane reads contiguous d values.  P.V: step r of key
+// block kb pairs the keys 32 kb + 8 (r/4) + 4 h + r%4 (h = lane half), which
+// is exactly what accumulator register r holds, so P needs no movement and V
+// stays row-major in LDS.
+
+// One online-softmax step over the 64 scores of this lane's row, exact for the
+// row maximum: score * mul is rounded on its own before the reference is
+// subtracted, so the maximal score maps to exactly exp2(0) = 1.
+template <int NOB>
+__device__ __forceinline__ void softmax_step_exact(f32x16 (&s)[2], RowState<NOB>& st, float mul) {
+  const float mx = tile_row_max(s) * mul;  // -inf stays -inf
+  if (wave_any(mx > st.m + kRescaleSlack)) rescale_row<NOB>(mx, st.m, st.l, st.o);
+  const float ref = st.m == -INFINITY ? 0.0f : st.m;
+  float sum = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float arg;
+      {
+#pragma clang fp contract(off)
+        const float t = s[kb][r] * mul;  // rounded on its own, not fused into the subtraction
+        arg = t - ref;
+      }
+      const float pr = __builtin_amdgcn_exp2f(arg);
+      s[kb][r] = pr;
+      sum += pr;
+    }
+  }
+  st.l += sum;
+}
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 2)))
@@ -532,14 +871,15 @@ void fwd32_kernel(FwdParams p) {
 
   Work w;
   if (!decode_work(p, w)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
+  const int h = w.h0;
   const int qrow = w.r0 + wid * 32 + ql;
 
   float qf[D / 2];
   {
     const float* qb = reinterpret_cast<const float*>(p.q) + (int64_t)w.b * p.q_bs +
-                      (int64_t)(w.q_start + qrow) * p.q_rs + (int64_t)w.h * p.q_hs + (D / 2) * hl;
+                      (int64_t)(w.q_start + qrow) * p.q_rs + (int64_t)h * p.q_hs + (D / 2) * hl;
 #pragma unroll
     for (int s = 0; s < D / 2; s += 4) {
       f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -554,7 +894,7 @@ void fwd32_kernel(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < NOB; ++i) st.o[i] = f32x16{};
 
-  const int rlast = min(w.r0 + kBlockM, w.Lq) - 1;
+  const int rlast = min(w.r0 + p.rows_per_wg, w.Lq) - 1;
   int kv_lo, kv_hi;
   key_range(p, w, w.r0, rlast, kv_lo, kv_hi);
   const int wa = w.r0 + wid * 32, wb = min(w.r0 + wid * 32 + 31, w.Lq - 1);
@@ -619,7 +959,7 @@ void fwd32_kernel(FwdParams p) {
                            (p.window > 0 && c0 < wb + off - p.window + 1);
     if (need_mask) mask_tile(s, c0, hl, qrow, off, w.Lk, upper, p.window);
 
-    softmax_step<NOB, true>(s, st, p.score_mul);
+    softmax_step_exact<NOB>(s, st, p.score_mul);
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -635,12 +975,24 @@ void fwd32_kernel(FwdParams p) {
     }
   }
 
-  store_rows<E_F32, D>(p, w, qrow, hl, st);
+  store_row<E_F32, D>(p, w, h, qrow, hl, st.m, st.l, st.o);
 }
 
 // ---------------------------------------------------------------------------
-// host launch
+// host planning and launch
 // ---------------------------------------------------------------------------
+
+bool plan_fwd(FwdParams& p, int elem, int head_dim) {
+  // every kernel: one head, 4 waves x 32 query rows per workgroup
+  p.heads_per_wg = 1;
+  p.rows_per_wg = 128;
+  const int64_t n_qtiles = ((int64_t)p.max_seqlen_q + p.rows_per_wg - 1) / p.rows_per_wg;
+  const int64_t n_groups = n_qtiles * p.batch * p.kv_heads;
+  if (n_groups > INT32_MAX / 8) return false;
+  p.n_qtiles = (int32_t)n_qtiles;
+  p.n_groups = (int32_t)n_groups;
+  return fwd_grid_size(p) <= (int64_t)UINT32_MAX / 2 && head_dim > 0;
+}
 
 hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t stream) {
   const int64_t grid = fwd_grid_size(p);
@@ -651,7 +1003,7 @@ hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t st
     switch (elem) {
       case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 128>)); break;
       case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 128>)); break;
-      case E_E4M3: VLGQA_LAUNCH((fwd16_kernel<E_E4M3, 128>)); break;
+      case E_E4M3: VLGQA_LAUNCH((fwd8_kernel<E_E4M3, 128>)); break;
       case E_F32: VLGQA_LAUNCH((fwd32_kernel<128>)); break;
       default: return hipErrorInvalidValue;
     }
@@ -659,7 +1011,7 @@ hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t st
     switch (elem) {
       case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 64>)); break;
       case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 64>)); break;
-      case E_E4M3: VLGQA_LAUNCH((fwd16_kernel<E_E4M3, 64>)); break;
+      case E_E4M3: VLGQA_LAUNCH((fwd8_kernel<E_E4M3, 64>)); break;
       case E_F32: VLGQA_LAUNCH((fwd32_kernel<64>)); break;
       default: return hipErrorInvalidValue;
     }

@@ -53,15 +53,12 @@ int elem_of_dtype(int dtype, int* elem) {
   }
 }
 
-// query tiles / groups / grid must fit the kernel's 32-bit work decode
 int finish_and_launch(vlgqa::FwdParams& p, int64_t max_seqlen_q, int elem, int64_t head_dim,
                       void* hip_stream) {
-  const int64_t n_qtiles = (max_seqlen_q + vlgqa::kBlockM - 1) / vlgqa::kBlockM;
-  const int64_t n_groups = n_qtiles * p.batch * p.kv_heads;
-  if (n_groups > INT32_MAX / 8 || n_groups * p.group > (int64_t)UINT32_MAX / 2)
+  if (max_seqlen_q > INT32_MAX) return fail(VLGQA_EINVAL, "max_seqlen_q", "too large");
+  p.max_seqlen_q = (int32_t)max_seqlen_q;
+  if (!vlgqa::plan_fwd(p, elem, (int)head_dim))
     return fail(VLGQA_EINVAL, "max_seqlen_q", "problem too large for one launch");
-  p.n_qtiles = (int32_t)n_qtiles;
-  p.n_groups = (int32_t)n_groups;
   hipError_t e = vlgqa::launch_fwd(p, elem, (int)head_dim, reinterpret_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
   return VLGQA_OK;

@@ -8,8 +8,7 @@ namespace vlgqa {
 // storage element kinds of q/k/v/out
 enum Elem : int { E_F32 = 0, E_F16 = 1, E_BF16 = 2, E_E4M3 = 3 };
 
-// query rows per workgroup (4 waves x 32 rows) and keys per K/V tile
-constexpr int kBlockM = 128;
+// keys per K/V tile and threads (4 waves) per workgroup
 constexpr int kBlockN = 64;
 constexpr int kThreads = 256;
 
@@ -30,8 +29,12 @@ struct FwdParams {
   int32_t batch, heads, kv_heads, group;
   int32_t seqlen_q, seqlen_k;  // dense extents (per-sequence lengths come from cu_* when given)
   int32_t causal, window;
-  int32_t n_qtiles;  // ceil(max_seqlen_q / kBlockM)
-  int32_t n_groups;  // n_qtiles * batch * kv_heads
+  int32_t max_seqlen_q;
+  // filled by plan_fwd for the kernel that runs:
+  int32_t heads_per_wg;  // query heads of one KV group handled by a workgroup (1 or 2)
+  int32_t rows_per_wg;   // query rows per head per workgroup
+  int32_t n_qtiles;      // ceil(max_seqlen_q / rows_per_wg)
+  int32_t n_groups;      // n_qtiles * batch * kv_heads
   float score_mul;   // multiplies q.k into the log2 domain: scale * log2(e) [* q_scale * k_scale]
   float out_mul;     // multiplies the normalised output: 1, or v_scale / o_scale for E4M3
 };
@@ -39,8 +42,12 @@ struct FwdParams {
 // Number of workgroups the forward launch uses for these parameters.
 inline int64_t fwd_grid_size(const FwdParams& p) {
   int64_t groups8 = ((int64_t)p.n_groups + 7) / 8 * 8;
-  return groups8 * p.group;
+  return groups8 * (p.group / p.heads_per_wg);
 }
+
+// Fills the launch-shape fields for the kernel that serves (elem, head_dim).
+// Returns false when the problem does not fit one launch.
+bool plan_fwd(FwdParams& p, int elem, int head_dim);
 
 hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t stream);
 
