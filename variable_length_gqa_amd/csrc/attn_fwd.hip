@@ -48,6 +48,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // this (log2 units); until then probabilities may reach 2^kRescaleSlack.  The
 // result is exact either way: numerator and denominator use the same reference.
 constexpr float kRescaleSlack = 8.0f;
+// bf16/f16 kernel: a lane's partial sum of probabilities (32 of them) may
+// reach this before the reference maximum is moved (probabilities <= 2^16).
+constexpr float kPartialSumBound = 65536.0f;
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -413,8 +416,7 @@ void fwd16_kernel(FwdParams p) {
   const int qrow = w.r0 + 32 * wid + ql;  // this lane's query row within the sequence
   const float mul = p.score_mul;
 
-  // Q^T fragments: lane holds q[qrow][16 ks + 8 hl .. +8]; only ever an MFMA
-  // operand, so it is parked in AGPRs (MFMA reads them directly)
+  // Q^T fragments: lane holds q[qrow][16 ks + 8 hl .. +8]
   u32x4 qf[C::NS];
   {
     const uint8_t* qbase = reinterpret_cast<const uint8_t*>(p.q) +
@@ -424,8 +426,6 @@ void fwd16_kernel(FwdParams p) {
     const uint32_t roff = (uint32_t)qrow * (uint32_t)(p.q_rs * 2);
 #pragma unroll
     for (int ks = 0; ks < C::NS; ++ks) qf[ks] = bload16(qr, roff + (16 * ks + 8 * hl) * 2);
-#pragma unroll
-    for (int ks = 0; ks < C::NS; ++ks) asm volatile("" : "=a"(qf[ks]) : "0"(qf[ks]));
   }
 
   // K/V of this (sequence, kv head): descriptors and per-thread tile offsets
@@ -513,9 +513,38 @@ void fwd16_kernel(FwdParams p) {
                              (p.window > 0 && c0 < wb + off - p.window + 1);
       if (need_mask) mask_tile(s, c0, hl, qrow, off, w.Lk, upper, p.window);
 
-      // online softmax over the row's 64 scores (32 here, 32 in lane ^ 32)
-      float mx;
-      {
+      // Online softmax over the row's 64 scores (32 here, 32 in lane ^ 32).
+      // Optimistic: exponentiate against the current reference maximum and
+      // move the reference only when some lane's partial sum exceeds 2^16
+      // (or is not finite) -- the first tile of a row, or a large jump.  Then
+      // the true tile maximum is taken, O and l are rescaled and the tile is
+      // exponentiated again.  Any reference gives the exact result (numerator
+      // and denominator share it); the bound only keeps P, l and O in range.
+      u32x4 pk[4];
+      float part;
+      auto exp_tile = [&](float ref) __attribute__((always_inline)) {
+        float sum0 = 0.0f, sum1 = 0.0f;
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) {
+          const f32x16& sb = s[t2 >> 1];
+          const int r = 8 * (t2 & 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r + 2 * i], mul, -ref));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r + 2 * i + 1], mul, -ref));
+            sum0 += p0;
+            sum1 += p1;
+            pk[t2][i] = pack2<ELEM>(p0, p1);
+          }
+        }
+        part = sum0 + sum1;
+      };
+      bool slow = wave_any(st.m == -INFINITY);
+      if (!slow) {
+        exp_tile(st.m);
+        slow = wave_any(!(part <= kPartialSumBound));
+      }
+      if (slow) {
         float a = __builtin_elementwise_maximum(s[0][0], s[1][0]);
         float b = __builtin_elementwise_maximum(s[0][1], s[1][1]);
 #pragma unroll
@@ -523,26 +552,16 @@ void fwd16_kernel(FwdParams p) {
           a = __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(s[0][r], s[1][r]));
           b = __builtin_elementwise_maximum(b, __builtin_elementwise_maximum(s[0][r + 1], s[1][r + 1]));
         }
-        mx = swap_halves_max(__builtin_elementwise_maximum(a, b)) * mul;
-      }
-      if (wave_any(mx > st.m + kRescaleSlack)) rescale_row<C::NOB>(mx, st.m, st.l, st.o);
-      const float ref = st.m == -INFINITY ? 0.0f : st.m;
-      u32x4 pk[4];
-      float sum0 = 0.0f, sum1 = 0.0f;
+        const float mx = swap_halves_max(__builtin_elementwise_maximum(a, b)) * mul;
+        const bool up = mx > st.m;  // -inf stays -inf
+        const float alpha = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.0f;
+        st.m = up ? mx : st.m;
+        st.l *= alpha;
 #pragma unroll
-      for (int t2 = 0; t2 < 4; ++t2) {
-        const f32x16& sb = s[t2 >> 1];
-        const int r = 8 * (t2 & 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r + 2 * i], mul, -ref));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r + 2 * i + 1], mul, -ref));
-          sum0 += p0;
-          sum1 += p1;
-          pk[t2][i] = pack2<ELEM>(p0, p1);
-        }
+        for (int i = 0; i < C::NOB; ++i) st.o[i] *= alpha;
+        exp_tile(st.m == -INFINITY ? 0.0f : st.m);
       }
-      st.l += sum0 + sum1;
+      st.l += part;
 
       // O^T += V^T P^T
 #pragma unroll
