@@ -301,8 +301,8 @@ struct KvSrc {
 // One workgroup = 128 query rows of one head, 4 waves x 32 rows; two
 // workgroups share a CU, so the two waves on a SIMD belong to independent
 // workgroups and one's vector work (softmax) overlaps the other's matrix work.
-// Per 64-key tile a wave does 16 MFMAs for S^T = K Q^T, the softmax of its
-// 32 x 64 scores, and 16 MFMAs for O^T += V^T P^T.
+// Per tile of BN keys a wave does BN/4 MFMAs for S^T = K Q^T, the softmax of
+// its 32 x BN scores, and BN/4 MFMAs for O^T += V^T P^T.
 //
 // K and V tiles reach LDS by DMA (buffer loads that write LDS directly: no
 // staging registers, no vector instructions), double-buffered: the next tile
@@ -321,13 +321,14 @@ struct KvSrc {
 // The buffer range of a (sequence, kv head) ends at its last key, so rows past
 // it arrive as zeros.
 
-template <int ELEM, int D>
+template <int ELEM, int D, int NKB>
 struct Cfg5 {
+  static constexpr int BN = 32 * NKB;                // keys per tile (NKB blocks of 32)
   static constexpr int NS = D / 16;                  // MFMA k-steps over d
   static constexpr int NOB = D / 32;                 // O^T accumulator blocks
   static constexpr int ROWB = D * 2;                 // bytes per K/V row in LDS
   static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
-  static constexpr int TILE = kBlockN * ROWB;        // bytes of one K (or V) tile
+  static constexpr int TILE = BN * ROWB;             // bytes of one K (or V) tile
   static constexpr int CPT = TILE / 16 / kThreads;   // DMA chunks per thread per tensor
   static_assert(CPT >= 1 && (TILE / 16) % kThreads == 0, "tile shape");
 };
@@ -370,10 +371,10 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
 // Request one tile (rows c0 .. c0+63) of K or V into an LDS tile buffer: this
 // thread's chunk n goes to LDS chunk (wid*CPT + n)*64 + lane, from tile offset
 // voff[n].  The instruction writes LDS only (no register results).
-template <int ELEM, int D>
+template <int ELEM, int D, int NKB>
 __device__ __forceinline__ void dma_tile(uint8_t* buf, u32x4 rsrc, uint32_t base, int wid,
-                                         const uint32_t (&voff)[Cfg5<ELEM, D>::CPT]) {
-  using C = Cfg5<ELEM, D>;
+                                         const uint32_t (&voff)[Cfg5<ELEM, D, NKB>::CPT]) {
+  using C = Cfg5<ELEM, D, NKB>;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)buf;
 #pragma unroll
   for (int n = 0; n < C::CPT; ++n) {
@@ -397,10 +398,29 @@ __device__ __forceinline__ u32x4 vt_operand(const uint8_t* p0, const uint8_t* p1
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
-template <int ELEM, int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+// Mask the S^T accumulators of the NKB 32-key blocks of a tile starting at key
+// c0 for the lane's query row q.  Key of register r in block kb: c0 + 32 kb +
+// 8 (r / 4) + 4 (lane / 32) + r % 4.
+template <int NKB>
+__device__ __forceinline__ void mask_blocks(f32x16 (&s)[NKB], int c0, int hl, int q, int off,
+                                            int Lk, bool upper, int window) {
+  const int hi = upper ? min(Lk - 1, q + off) : Lk - 1;
+  const int lo = window > 0 ? q + off - window + 1 : 0;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = c0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+      if (key > hi || key < lo) s[kb][r] = -INFINITY;
+    }
+  }
+}
+
+template <int ELEM, int D, int NKB, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(WPE, WPE)))
 void fwd16_kernel(FwdParams p) {
-  using C = Cfg5<ELEM, D>;
+  using C = Cfg5<ELEM, D, NKB>;
+  constexpr int BN = C::BN;
   constexpr int OUT = ELEM;
   __shared__ __attribute__((aligned(1024))) uint8_t lk0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lk1[C::TILE];
@@ -471,8 +491,8 @@ void fwd16_kernel(FwdParams p) {
   const bool upper = p.causal || p.window > 0;
   int kv_lo, kv_hi;
   key_range(p, w, w.r0, min(w.r0 + p.rows_per_wg, w.Lq) - 1, kv_lo, kv_hi);
-  const int t0 = kv_lo / kBlockN;
-  const int t1 = kv_hi > kv_lo ? (kv_hi + kBlockN - 1) / kBlockN : t0;
+  const int t0 = kv_lo / BN;
+  const int t1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : t0;
   const int wa = w.r0 + 32 * wid, wb = min(wa + 31, w.Lq - 1);
   int wlo = 0, whi = 0;
   if (wa <= wb) key_range(p, w, wa, wb, wlo, whi);
@@ -484,8 +504,8 @@ void fwd16_kernel(FwdParams p) {
   for (int i = 0; i < C::NOB; ++i) st.o[i] = f32x16{};
 
   if (t0 < t1) {
-    dma_tile<ELEM, D>(lk0, krs, (uint32_t)(t0 * kBlockN) * rs, wid, voff);
-    dma_tile<ELEM, D>(lv0, vrs, (uint32_t)(t0 * kBlockN) * rs, wid, voff);
+    dma_tile<ELEM, D, NKB>(lk0, krs, (uint32_t)(t0 * BN) * rs, wid, voff);
+    dma_tile<ELEM, D, NKB>(lv0, vrs, (uint32_t)(t0 * BN) * rs, wid, voff);
   }
   wait_vm_all();
   lds_barrier();
@@ -493,25 +513,28 @@ void fwd16_kernel(FwdParams p) {
   auto tile = [&](int t, const uint8_t* kb_, const uint8_t* vb_, uint8_t* knext,
                   uint8_t* vnext) __attribute__((always_inline)) {
     if (t + 1 < t1) {
-      const uint32_t base = (uint32_t)((t + 1) * kBlockN) * rs;
-      dma_tile<ELEM, D>(knext, krs, base, wid, voff);
-      dma_tile<ELEM, D>(vnext, vrs, base, wid, voff);
+      const uint32_t base = (uint32_t)((t + 1) * BN) * rs;
+      dma_tile<ELEM, D, NKB>(knext, krs, base, wid, voff);
+      dma_tile<ELEM, D, NKB>(vnext, vrs, base, wid, voff);
     }
-    const int c0 = t * kBlockN;
-    if (wa <= wb && c0 < whi && c0 + kBlockN > wlo) {
+    const int c0 = t * BN;
+    if (wa <= wb && c0 < whi && c0 + BN > wlo) {
       // S^T = K Q^T for the two 32-key blocks
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::NS; ++ks) {
         const uint32_t ko = koff0 ^ (uint32_t)(ks << 5);
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kb_ + ko);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kb_ + ko + 32 * C::ROWB);
-        s[0] = mfma16<ELEM>(a0, qf[ks], s[0]);
-        s[1] = mfma16<ELEM>(a1, qf[ks], s[1]);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kb_ + ko + kb * 32 * C::ROWB);
+          s[kb] = mfma16<ELEM>(a, qf[ks], s[kb]);
+        }
       }
-      const bool need_mask = (c0 + kBlockN > w.Lk) || (upper && c0 + kBlockN - 1 > wa + off) ||
+      const bool need_mask = (c0 + BN > w.Lk) || (upper && c0 + BN - 1 > wa + off) ||
                              (p.window > 0 && c0 < wb + off - p.window + 1);
-      if (need_mask) mask_tile(s, c0, hl, qrow, off, w.Lk, upper, p.window);
+      if (need_mask) mask_blocks<NKB>(s, c0, hl, qrow, off, w.Lk, upper, p.window);
 
       // Online softmax over the row's 64 scores (32 here, 32 in lane ^ 32).
       // Optimistic: exponentiate against the current reference maximum and
@@ -520,12 +543,12 @@ void fwd16_kernel(FwdParams p) {
       // the true tile maximum is taken, O and l are rescaled and the tile is
       // exponentiated again.  Any reference gives the exact result (numerator
       // and denominator share it); the bound only keeps P, l and O in range.
-      u32x4 pk[4];
+      u32x4 pk[2 * NKB];
       float part;
       auto exp_tile = [&](float ref) __attribute__((always_inline)) {
         float sum0 = 0.0f, sum1 = 0.0f;
 #pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2) {
+        for (int t2 = 0; t2 < 2 * NKB; ++t2) {
           const f32x16& sb = s[t2 >> 1];
           const int r = 8 * (t2 & 1);
 #pragma unroll
@@ -545,12 +568,14 @@ void fwd16_kernel(FwdParams p) {
         slow = wave_any(!(part <= kPartialSumBound));
       }
       if (slow) {
-        float a = __builtin_elementwise_maximum(s[0][0], s[1][0]);
-        float b = __builtin_elementwise_maximum(s[0][1], s[1][1]);
+        float a = s[0][0], b = s[0][1];
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) {
-          a = __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(s[0][r], s[1][r]));
-          b = __builtin_elementwise_maximum(b, __builtin_elementwise_maximum(s[0][r + 1], s[1][r + 1]));
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int r = kb == 0 ? 2 : 0; r < 16; r += 2) {
+            a = __builtin_elementwise_maximum(a, s[kb][r]);
+            b = __builtin_elementwise_maximum(b, s[kb][r + 1]);
+          }
         }
         const float mx = swap_halves_max(__builtin_elementwise_maximum(a, b)) * mul;
         const bool up = mx > st.m;  // -inf stays -inf
@@ -565,7 +590,7 @@ void fwd16_kernel(FwdParams p) {
 
       // O^T += V^T P^T
 #pragma unroll
-      for (int t2 = 0; t2 < 4; ++t2) {
+      for (int t2 = 0; t2 < 2 * NKB; ++t2) {
 #pragma unroll
         for (int db = 0; db < C::NOB; ++db) {
           const u32x4 a = vt_operand(vb_ + voffs[db][0] + t2 * 16 * C::ROWB,
@@ -1013,6 +1038,15 @@ bool plan_fwd(FwdParams& p, int elem, int head_dim) {
   return fwd_grid_size(p) <= (int64_t)UINT32_MAX / 2 && head_dim > 0;
 }
 
+#ifndef VLGQA_NKB
+#define VLGQA_NKB 1
+#endif
+#ifndef VLGQA_WPE
+#define VLGQA_WPE 3
+#endif
+constexpr int kNkb = VLGQA_NKB;  // 32-key blocks per tile of the bf16/f16 kernel
+constexpr int kWpe = VLGQA_WPE;  // its waves per SIMD
+
 hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t stream) {
   const int64_t grid = fwd_grid_size(p);
   if (grid <= 0) return hipSuccess;
@@ -1020,16 +1054,16 @@ hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t st
 #define VLGQA_LAUNCH(KERNEL) hipLaunchKernelGGL((KERNEL), g, b, 0, stream, p)
   if (head_dim == 128) {
     switch (elem) {
-      case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 128>)); break;
-      case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 128>)); break;
+      case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 128, kNkb, kWpe>)); break;
+      case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 128, kNkb, kWpe>)); break;
       case E_E4M3: VLGQA_LAUNCH((fwd8_kernel<E_E4M3, 128>)); break;
       case E_F32: VLGQA_LAUNCH((fwd32_kernel<128>)); break;
       default: return hipErrorInvalidValue;
     }
   } else if (head_dim == 64) {
     switch (elem) {
-      case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 64>)); break;
-      case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 64>)); break;
+      case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 64, kNkb, kWpe>)); break;
+      case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 64, kNkb, kWpe>)); break;
       case E_E4M3: VLGQA_LAUNCH((fwd8_kernel<E_E4M3, 64>)); break;
       case E_F32: VLGQA_LAUNCH((fwd32_kernel<64>)); break;
       default: return hipErrorInvalidValue;
