@@ -555,19 +555,15 @@ void fwd16_kernel(FwdParams p) {
           for (int i = 0; i < 4; ++i) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r + 2 * i], mul, -ref));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r + 2 * i + 1], mul, -ref));
-            sum0 += p0;
-            sum1 += p1;
+            sum0 = (t2 == 0 && i == 0) ? p0 : sum0 + p0;
+            sum1 = (t2 == 0 && i == 0) ? p1 : sum1 + p1;
             pk[t2][i] = pack2<ELEM>(p0, p1);
           }
         }
         part = sum0 + sum1;
       };
-      bool slow = wave_any(st.m == -INFINITY);
-      if (!slow) {
-        exp_tile(st.m);
-        slow = wave_any(!(part <= kPartialSumBound));
-      }
-      if (slow) {
+      exp_tile(st.m);  // a row's first tile (m = -inf) gives a non-finite sum
+      if (wave_any(!(part <= kPartialSumBound))) {
         float a = s[0][0], b = s[0][1];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
