@@ -39,5 +39,6 @@ from .attention import (  # noqa: F401
     flash_attention_fwd_fp8,
     varlen_rows,
     dense_rows,
+    fp8_rows,
 )
 from . import brute, online, e4m3  # noqa: F401
