@@ -191,7 +191,12 @@ def check_fp8(d, o_scale=None):
     amax = float(np.abs(O).max())
     assert_close("O(fp8)", got, O, FP8_REL_TOL * amax)
     assert_close("LSE", lse.cpu().double().numpy(), L, FP8_LSE_TOL)
-    # most codes agree exactly with the oracle's own rounding of O / o_scale
+    # P is rounded to bf16 and V is exact, so O is within a few bf16 roundings
+    # of the oracle and most codes agree exactly with the oracle's own
+    # rounding of O / o_scale; the mean error is a small fraction of a code
+    # spacing (rounding P to E4M3 instead gives ~60% agreement)
+    err = np.abs(got - O)
+    assert err.mean() <= 1e-2 * amax, err.mean() / amax
     agree = float((out.cpu().numpy() == o8).mean())
     assert agree > 0.9, agree
     return out

@@ -95,41 +95,17 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
-// OCP E4M3 code (low 8 bits of c) -> bf16 bits, exact.  NaN codes map to NaN.
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
-  uint32_t s = (c & 0x80u) << 8;
-  uint32_t em = c & 0x7Fu;
-  uint32_t normal = (em + (120u << 3)) << 4;                       // exponent e -> e + 120
-  uint32_t sub = __float_as_uint((float)em * 0.001953125f) >> 16;  // m * 2^-9, exact in bf16
-  uint32_t r = em >= 8u ? normal : sub;
-  r = em == 0x7Fu ? 0x7FC0u : r;
-  return s | r;
+// four floats -> four OCP E4M3 codes in one register (v_cvt_pk_fp8_f32: round
+// to nearest even).  Callers keep |x| <= 448 (the largest finite code).
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
 }
 
-// 4 E4M3 codes (one u32) -> 4 bf16 (two u32)
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
-  u32x2 r;
-  r[0] = e4m3_to_bf16(w & 0xFF) | (e4m3_to_bf16((w >> 8) & 0xFF) << 16);
-  r[1] = e4m3_to_bf16((w >> 16) & 0xFF) | (e4m3_to_bf16(w >> 24) << 16);
-  return r;
-}
-
-// f32 -> OCP E4M3 code, round to nearest even, saturating at +-448.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  uint32_t u = __float_as_uint(x);
-  uint32_t s = (u >> 24) & 0x80u;
-  float a = fabsf(x);
-  if (a != a) return 0x7Fu;
-  if (a >= 448.0f) return s | 0x7Eu;
-  if (a < 0.015625f) {  // subnormal range: spacing 2^-9 (8 lands on the smallest normal)
-    return s | (uint32_t)__builtin_rintf(a * 512.0f);
-  }
-  uint32_t ua = __float_as_uint(a);
-  ua += 0x7FFFFu + ((ua >> 20) & 1u);  // round the f32 mantissa to 3 bits, ties to even
-  uint32_t e = (ua >> 23) - 120u;      // e4m3 exponent field (bias 7)
-  uint32_t m = (ua >> 20) & 7u;
-  if (e > 15u || (e == 15u && m == 7u)) return s | 0x7Eu;
-  return s | (e << 3) | m;
+// clamp to the finite E4M3 range (saturating encode: never a NaN code)
+__device__ __forceinline__ float sat448(float x) {
+  return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -194,9 +170,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 __device__ __forceinline__ uint32_t sat_bytes(int64_t b) {
   return b > 0xFFFFFFFFll ? 0xFFFFFFFFu : (b < 0 ? 0u : (uint32_t)b);
@@ -274,8 +247,7 @@ __device__ __forceinline__ void store_row(const FwdParams& p, const Work& w, int
         f32x4 v = {x0, x1, x2, x3};
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d0) = v;
       } else if constexpr (OUT_ELEM == E_E4M3) {
-        uint32_t v = f32_to_e4m3(x0) | (f32_to_e4m3(x1) << 8) | (f32_to_e4m3(x2) << 16) |
-                     (f32_to_e4m3(x3) << 24);
+        const uint32_t v = pack4_fp8(sat448(x0), sat448(x1), sat448(x2), sat448(x3));
         *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.o) + orow + d0) = v;
       } else {
         u32x2 v = {pack2<OUT_ELEM>(x0, x1), pack2<OUT_ELEM>(x2, x3)};
@@ -288,11 +260,6 @@ __device__ __forceinline__ void store_row(const FwdParams& p, const Work& w, int
     p.lse[(int64_t)w.b * p.l_bs + (int64_t)(w.q_start + qrow) * p.l_rs + (int64_t)h * p.l_hs] = lse;
   }
 }
-
-struct KvSrc {
-  __amdgpu_buffer_rsrc_t k, v;  // this (sequence, kv head)'s K/V, range = its Lk rows
-  uint32_t rs;                  // row stride in bytes
-};
 
 // ---------------------------------------------------------------------------
 // bf16 / f16 kernel
@@ -400,19 +367,30 @@ __device__ __forceinline__ u32x4 vt_operand(const uint8_t* p0, const uint8_t* p1
 
 // Mask the S^T accumulators of the NKB 32-key blocks of a tile starting at key
 // c0 for the lane's query row q.  Key of register r in block kb: c0 + 32 kb +
-// 8 (r / 4) + 4 (lane / 32) + r % 4.
+// kk(r) + 4 (lane / 32) with kk(r) = 8 (r / 4) + r % 4, so each test is one
+// compare of a constant against a per-lane bound.
 template <int NKB>
 __device__ __forceinline__ void mask_blocks(f32x16 (&s)[NKB], int c0, int hl, int q, int off,
                                             int Lk, bool upper, int window) {
-  const int hi = upper ? min(Lk - 1, q + off) : Lk - 1;
-  const int lo = window > 0 ? q + off - window + 1 : 0;
+  const int base = c0 + 4 * hl;
+  const int a = (upper ? min(Lk - 1, q + off) : Lk - 1) - base;  // visible iff key' <= a
+  if (window > 0) {
+    const int b = q + off - window + 1 - base;                   // ... and key' >= b
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = c0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-      if (key > hi || key < lo) s[kb][r] = -INFINITY;
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 32 * kb + 8 * (r >> 2) + (r & 3);
+        if (kk > a || kk < b) s[kb][r] = -INFINITY;
+      }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 32 * kb + 8 * (r >> 2) + (r & 3);
+        if (kk > a) s[kb][r] = -INFINITY;
+      }
   }
 }
 
@@ -610,257 +588,280 @@ void fwd16_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// E4M3 kernel: codes widened to bf16 on the way into LDS, 32 rows per wave
+// E4M3 kernel: S^T on the FP8 matrix cores, P V in bf16
 // ---------------------------------------------------------------------------
 //
-// One workgroup = 128 query rows of one head, 4 waves x 32 rows, two
-// workgroups per CU.  K/V tiles of 64 keys go global -> registers (one tile
-// ahead) -> LDS (double buffered): K row-major, V transposed (a 4x8 register
-// transpose) with the middle two 4-key quads of every 16 keys swapped to match
-// the order of the P operand.  E4M3 values are exact in bf16, so the widening
-// loses nothing; the per-tensor scales are folded into the score multiplier
-// and the output multiplier.
+// The structure of the 16-bit kernel (128 query rows per workgroup, 4 waves x
+// 32 rows, 32-key tiles, double-buffered LDS, one LDS-only barrier per tile),
+// with two changes:
+//   S^T = K Q^T runs on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, f32
+//     accumulation; a lane holds row l % 32 and the 32 consecutive k elements
+//     from 32 (l / 32)): A = K codes from LDS (two 16-byte reads), B = Q^T codes
+//     kept in registers.  The per-tensor scales q_scale k_scale / sqrt(D) (times
+//     log2 e) multiply the f32 scores.  K reaches LDS by DMA, unconverted.
+//   P V stays on the bf16 matrix cores with P rounded to bf16: rounding P to
+//     E4M3 instead (3 mantissa bits) moves O by up to ~2.5% of max|O| on
+//     long, flat rows, which with the E4M3 rounding of the output exceeds the
+//     6e-2 * max|O| tolerance.  V codes are loaded to registers one tile ahead,
+//     widened to bf16 (exact: every E4M3 value is a bf16 value) with
+//     v_cvt_scalef32_pk_bf16_fp8, and written to LDS in the 16-bit kernel's
+//     swizzled row layout, so the same transposing reads build V^T.
+// The epilogue multiplies by v_scale / o_scale and encodes E4M3 with round to
+// nearest even, saturating at +-448.
 
-template <int NOB>
-__device__ __forceinline__ void softmax_step8(f32x16 (&s)[2], RowState<NOB>& st, float mul) {
-  const float mx = tile_row_max(s) * mul;  // -inf stays -inf
-  if (wave_any(mx > st.m + kRescaleSlack)) rescale_row<NOB>(mx, st.m, st.l, st.o);
-  const float ref = st.m == -INFINITY ? 0.0f : st.m;
-  float sum = 0.0f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], mul, -ref));
-      s[kb][r] = pr;
-      sum += pr;
-    }
-  }
-  st.l += sum;
-}
-
-template <int ELEM, int D>
-struct Tile8 {
-  static constexpr int KP = D + 8;          // K row pitch in LDS (u16), 16 B pad
-  static constexpr int VP = kBlockN + 8;    // V^T row pitch in LDS (u16)
-  static constexpr int EB = ELEM == E_E4M3 ? 1 : 2;  // stored bytes per element
-  // K: 16-byte global chunks
-  static constexpr int K_CPR = D * EB / 16;                   // chunks per key row
-  static constexpr int K_CPT = kBlockN * K_CPR / kThreads;    // chunks per thread
-  // V: units of 4 keys x 8 d
-  static constexpr int V_UNITS = (kBlockN / 4) * (D / 8);
-  static_assert(K_CPT >= 1 && V_UNITS <= kThreads, "tile shape");
+template <int D>
+struct Cfg8 {
+  static constexpr int BN = 32;                      // keys per tile
+  static constexpr int NS = D / 64;                  // 64-deep k-steps of S^T over d
+  static constexpr int NOB = D / 32;                 // O^T accumulator blocks
+  static constexpr int KROWB = D;                    // bytes per E4M3 K row in LDS
+  static constexpr int KCPR = KROWB / 16;            // 16-byte chunks per K row
+  static constexpr int KTILE = BN * KROWB;           // bytes of one K tile
+  static constexpr int NCH = KTILE / 16;             // 16-byte chunks per K (or E4M3 V) tile
+  static constexpr int VROWB = 2 * D;                // bytes per bf16 V row in LDS
+  static constexpr int VTILE = BN * VROWB;           // bytes of one bf16 V tile
+  static_assert(NCH <= kThreads && NCH % 64 == 0, "tile shape");
 };
 
-template <int ELEM, int D>
-struct Staging8 {
-  u32x4 k[Tile8<ELEM, D>::K_CPT];
-  u32x4 v[4];  // 4 key rows x 8 d (E4M3: only the low 2 words used)
-};
-
-template <int ELEM, int D>
-__device__ __forceinline__ void load_tile8(const FwdParams& p, const Work& w, int c0, int tid,
-                                            Staging8<ELEM, D>& st) {
-  using T = Tile8<ELEM, D>;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) +
-                         ((int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs + (int64_t)w.kvh * p.k_hs) * T::EB;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) +
-                         ((int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs + (int64_t)w.kvh * p.k_hs) * T::EB;
-  const int64_t rs = p.k_rs * T::EB;
-#pragma unroll
-  for (int c = 0; c < T::K_CPT; ++c) {
-    const int idx = c * kThreads + tid;
-    const int row = idx / T::K_CPR, col = idx % T::K_CPR;
-    const int key = c0 + row;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (key < w.Lk) z = *reinterpret_cast<const u32x4*>(kbase + key * rs + col * 16);
-    st.k[c] = z;
-  }
-  if (tid < T::V_UNITS) {
-    // key quad fastest across lanes: the transposed LDS writes of 16 lanes then
-    // fill 16 different 8-byte slots of one V^T row (no bank conflicts)
-    const int kq = tid % (kBlockN / 4), db = tid / (kBlockN / 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = c0 + 4 * kq + j;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (key < w.Lk) {
-        if constexpr (T::EB == 2) {
-          z = *reinterpret_cast<const u32x4*>(vbase + key * rs + db * 16);
-        } else {
-          u32x2 t = *reinterpret_cast<const u32x2*>(vbase + key * rs + db * 8);
-          z[0] = t[0];
-          z[1] = t[1];
-        }
-      }
-      st.v[j] = z;
-    }
-  }
+// chunk swizzle of an E4M3 K row in LDS: the 16 lanes of a K read cover 16
+// consecutive rows of one logical chunk; the swizzle is a bijection on the
+// rows of equal parity (D=128, 8 chunks a row) or equal residue mod 4 (D=64,
+// 4 chunks), so the 16 reads fall in distinct banks.
+template <int D>
+__device__ __forceinline__ int swz8(int row) {
+  if constexpr (D == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
 }
 
-template <int ELEM, int D>
-__device__ __forceinline__ void store_tile8(uint16_t* sK, uint16_t* sV, int tid,
-                                             const Staging8<ELEM, D>& st) {
-  using T = Tile8<ELEM, D>;
-#pragma unroll
-  for (int c = 0; c < T::K_CPT; ++c) {
-    const int idx = c * kThreads + tid;
-    const int row = idx / T::K_CPR, col = idx % T::K_CPR;
-    if constexpr (T::EB == 2) {
-      *reinterpret_cast<u32x4*>(sK + row * T::KP + col * 8) = st.k[c];
-    } else {  // 16 codes -> 16 bf16
-      u32x2 a = e4m3x4_to_bf16(st.k[c][0]), b = e4m3x4_to_bf16(st.k[c][1]);
-      u32x2 e = e4m3x4_to_bf16(st.k[c][2]), f = e4m3x4_to_bf16(st.k[c][3]);
-      u32x4 lo = {a[0], a[1], b[0], b[1]}, hi = {e[0], e[1], f[0], f[1]};
-      *reinterpret_cast<u32x4*>(sK + row * T::KP + col * 16) = lo;
-      *reinterpret_cast<u32x4*>(sK + row * T::KP + col * 16 + 8) = hi;
-    }
-  }
-  if (tid < T::V_UNITS) {
-    const int kq = tid % (kBlockN / 4), db = tid / (kBlockN / 4);
-    // rows j = 0..3 (keys 4kq + j) as 8 x 16-bit each: w[j][i] holds d = 2i, 2i+1
-    uint32_t w[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (T::EB == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[j][i] = st.v[j][i];
-      } else {
-        u32x2 a = e4m3x4_to_bf16(st.v[j][0]), b = e4m3x4_to_bf16(st.v[j][1]);
-        w[j][0] = a[0]; w[j][1] = a[1]; w[j][2] = b[0]; w[j][3] = b[1];
-      }
-    }
-    // key quad kq of the tile -> LDS position quad (middle quads of each 16 swapped)
-    const int qq = kq & 3;
-    const int pq = (kq & ~3) | (qq == 1 ? 2 : (qq == 2 ? 1 : qq));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // d = db*8 + 2i: low halves; d = db*8 + 2i + 1: high halves
-      u32x2 ev, od;
-      ev[0] = __builtin_amdgcn_perm(w[1][i], w[0][i], 0x05040100u);
-      ev[1] = __builtin_amdgcn_perm(w[3][i], w[2][i], 0x05040100u);
-      od[0] = __builtin_amdgcn_perm(w[1][i], w[0][i], 0x07060302u);
-      od[1] = __builtin_amdgcn_perm(w[3][i], w[2][i], 0x07060302u);
-      *reinterpret_cast<u32x2*>(sV + (db * 8 + 2 * i) * T::VP + pq * 4) = ev;
-      *reinterpret_cast<u32x2*>(sV + (db * 8 + 2 * i + 1) * T::VP + pq * 4) = od;
-    }
-  }
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma_fp8(const u32x4 (&a)[2], const u32x4 (&b)[2], f32x16 c) {
+  const i32x8 av = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3],
+                    (int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
+  const i32x8 bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
+                    (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
+  // format selectors 0/0: both operands OCP E4M3; zero block scales = no scaling
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
 }
 
-template <int ELEM, int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+// two E4M3 codes (bytes 0-1 or 2-3 of w) -> two bf16 in one register, exact
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  const bf16x2_t r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void fwd8_kernel(FwdParams p) {
-  using T = Tile8<ELEM, D>;
-  constexpr int NS = D / 16;   // MFMA k-steps over d
-  constexpr int NOB = D / 32;  // O^T accumulator blocks
-  constexpr int OUT = ELEM;    // output stored in the input format
-
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlockN * T::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * T::VP];
+  using C = Cfg8<D>;
+  using V16 = Cfg5<E_BF16, D, 1>;  // the bf16 V tile layout of the 16-bit kernel
+  constexpr int BN = C::BN;
+  static_assert(V16::TILE == C::VTILE, "V tile");
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[C::KTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk1[C::KTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv0[C::VTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv1[C::VTILE];
 
   Work w;
   if (!decode_work(p, w)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
-  const int qrow = w.r0 + wid * 32 + ql;  // this lane's query row within the sequence
+  const int h = w.h0;
+  const int qrow = w.r0 + 32 * wid + ql;
+  const float mul = p.score_mul;
 
-  // Q^T fragments: lane holds q[qrow][16 s + 8 hl .. +8]
-  u32x4 qf[NS];
+  // Q^T codes: lane holds q[qrow][64 ks + 32 hl .. +32]
+  u32x4 qf[C::NS][2];
   {
-    const uint8_t* qb = reinterpret_cast<const uint8_t*>(p.q) +
-                        ((int64_t)w.b * p.q_bs + (int64_t)(w.q_start + qrow) * p.q_rs +
-                         (int64_t)w.h0 * p.q_hs) * T::EB;
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(p.q) +
+                           ((int64_t)w.b * p.q_bs + (int64_t)w.q_start * p.q_rs +
+                            (int64_t)h * p.q_hs);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qbase, sat_bytes((int64_t)w.Lq * p.q_rs));
+    const uint32_t roff = (uint32_t)qrow * (uint32_t)p.q_rs;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (qrow < w.Lq) {
-        if constexpr (T::EB == 2) {
-          z = *reinterpret_cast<const u32x4*>(qb + (16 * s + 8 * hl) * 2);
-        } else {
-          u32x2 c = *reinterpret_cast<const u32x2*>(qb + 16 * s + 8 * hl);
-          u32x2 a = e4m3x4_to_bf16(c[0]), bb = e4m3x4_to_bf16(c[1]);
-          z[0] = a[0]; z[1] = a[1]; z[2] = bb[0]; z[3] = bb[1];
-        }
-      }
-      qf[s] = z;
+    for (int ks = 0; ks < C::NS; ++ks) {
+      qf[ks][0] = bload16(qr, roff + 64 * ks + 32 * hl);
+      qf[ks][1] = bload16(qr, roff + 64 * ks + 32 * hl + 16);
     }
   }
 
-  RowState<NOB> st;
+  // K/V of this (sequence, kv head)
+  u32x4 krs;
+  __amdgpu_buffer_rsrc_t vr;
+  uint32_t rs;
+  {
+    const int64_t koff = (int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs +
+                         (int64_t)w.kvh * p.k_hs;
+    const uint32_t bytes = sat_bytes((int64_t)w.Lk * p.k_rs);
+    krs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
+    vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
+    rs = (uint32_t)p.k_rs;
+  }
+  // this thread's 16-byte chunk of a K (or E4M3 V) tile, if any (wave-uniform)
+  const bool has_chunk = wid * 64 < C::NCH;
+  const int crow = tid / C::KCPR, cch = tid % C::KCPR;
+  const uint32_t kdma = (uint32_t)crow * rs + (uint32_t)((cch ^ swz8<D>(crow)) * 16);
+  const uint32_t vld = (uint32_t)crow * rs + (uint32_t)cch * 16;
+  //  ... whose 16 bf16 go to logical chunks 2 cch, 2 cch + 1 of V row crow
+  const uint32_t vst0 = (uint32_t)crow * C::VROWB + (uint32_t)(((2 * cch) ^ swz<D>(crow)) * 16);
+  const uint32_t vst1 = (uint32_t)crow * C::VROWB + (uint32_t)(((2 * cch + 1) ^ swz<D>(crow)) * 16);
+  auto dma_k = [&](uint8_t* buf, uint32_t base) __attribute__((always_inline)) {
+    if (has_chunk) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(lds_void*)buf + wid * 1024);
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds"
+          :
+          : "s"(dst), "v"(base + kdma), "s"(krs)
+          : "memory", "m0");
+    }
+  };
+  auto store_v = [&](uint8_t* buf, u32x4 c) __attribute__((always_inline)) {
+    if (has_chunk) {
+      const u32x4 lo = {fp8x2_to_bf16x2(c[0], false), fp8x2_to_bf16x2(c[0], true),
+                        fp8x2_to_bf16x2(c[1], false), fp8x2_to_bf16x2(c[1], true)};
+      const u32x4 hi = {fp8x2_to_bf16x2(c[2], false), fp8x2_to_bf16x2(c[2], true),
+                        fp8x2_to_bf16x2(c[3], false), fp8x2_to_bf16x2(c[3], true)};
+      *reinterpret_cast<u32x4*>(buf + vst0) = lo;
+      *reinterpret_cast<u32x4*>(buf + vst1) = hi;
+    }
+  };
+  // LDS read offsets (tile-relative):
+  //  K for step ks: row ql, chunks 4 ks + 2 hl and 4 ks + 2 hl + 1
+  uint32_t koffs[C::NS][2];
+#pragma unroll
+  for (int ks = 0; ks < C::NS; ++ks)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      koffs[ks][c] = (uint32_t)ql * C::KROWB + (uint32_t)(((4 * ks + 2 * hl + c) ^ swz8<D>(ql)) * 16);
+  //  V^T operands: as in the 16-bit kernel
+  uint32_t voffs[C::NOB][2];
+  {
+    const int g = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
+#pragma unroll
+    for (int db = 0; db < C::NOB; ++db)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = 8 * c + 4 * (g >> 1) + e;
+        const int ch = 4 * db + 2 * (g & 1) + (j >> 1);
+        voffs[db][c] = (uint32_t)row * C::VROWB + (uint32_t)((ch ^ swz<D>(row)) * 16) + (j & 1) * 8;
+      }
+  }
+
+  const int off = w.Lk - w.Lq;
+  const bool upper = p.causal || p.window > 0;
+  int kv_lo, kv_hi;
+  key_range(p, w, w.r0, min(w.r0 + p.rows_per_wg, w.Lq) - 1, kv_lo, kv_hi);
+  const int t0 = kv_lo / BN;
+  const int t1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : t0;
+  const int wa = w.r0 + 32 * wid, wb = min(wa + 31, w.Lq - 1);
+  int wlo = 0, whi = 0;
+  if (wa <= wb) key_range(p, w, wa, wb, wlo, whi);
+
+  RowState<C::NOB> st;
   st.m = -INFINITY;
   st.l = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NOB; ++i) st.o[i] = f32x16{};
+  for (int i = 0; i < C::NOB; ++i) st.o[i] = f32x16{};
 
-  const int rlast = min(w.r0 + p.rows_per_wg, w.Lq) - 1;
-  int kv_lo, kv_hi;
-  key_range(p, w, w.r0, rlast, kv_lo, kv_hi);
-  // this wave's rows and keys
-  const int wa = w.r0 + wid * 32, wb = min(w.r0 + wid * 32 + 31, w.Lq - 1);
-  int wlo, whi;
-  key_range(p, w, wa, wb, wlo, whi);
-  const bool wave_live = wa <= wb;
-  const int off = w.Lk - w.Lq;
-  const bool upper = p.causal || p.window > 0;
+  if (t0 < t1) {
+    dma_k(lk0, (uint32_t)(t0 * BN) * rs);
+    u32x4 vc = has_chunk ? bload16(vr, (uint32_t)(t0 * BN) * rs + vld) : u32x4{};
+    wait_vm_all();
+    store_v(lv0, vc);
+  }
+  lds_barrier();
 
-  const int t0 = kv_lo / kBlockN;
-  const int t1 = kv_hi > kv_lo ? (kv_hi + kBlockN - 1) / kBlockN : t0;
-
-  Staging8<ELEM, D> stg;
-  if (t0 < t1) load_tile8<ELEM, D>(p, w, t0 * kBlockN, tid, stg);
-
-  for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
-    uint16_t* k_s = sK[buf];
-    uint16_t* v_s = sV[buf];
-    store_tile8<ELEM, D>(k_s, v_s, tid, stg);
-    __syncthreads();
-    if (t + 1 < t1) load_tile8<ELEM, D>(p, w, (t + 1) * kBlockN, tid, stg);
-
-    const int c0 = t * kBlockN;
-    if (!wave_live || c0 >= whi || c0 + kBlockN <= wlo) continue;
-
-    // S^T = K Q^T for two 32-key blocks
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < NS; ++ks) {
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(k_s + ql * T::KP + 16 * ks + 8 * hl);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(k_s + (32 + ql) * T::KP + 16 * ks + 8 * hl);
-      s[0] = mfma16<ELEM>(a0, qf[ks], s[0]);
-      s[1] = mfma16<ELEM>(a1, qf[ks], s[1]);
+  auto tile = [&](int t, const uint8_t* kb_, const uint8_t* vb_, uint8_t* knext,
+                  uint8_t* vnext) __attribute__((always_inline)) {
+    const bool more = t + 1 < t1;
+    u32x4 vc = {};
+    if (more) {
+      const uint32_t base = (uint32_t)((t + 1) * BN) * rs;
+      dma_k(knext, base);
+      if (has_chunk) vc = bload16(vr, base + vld);
     }
+    const int c0 = t * BN;
+    if (wa <= wb && c0 < whi && c0 + BN > wlo) {
+      f32x16 s[1] = {f32x16{}};
+#pragma unroll
+      for (int ks = 0; ks < C::NS; ++ks) {
+        const u32x4 a[2] = {*reinterpret_cast<const u32x4*>(kb_ + koffs[ks][0]),
+                            *reinterpret_cast<const u32x4*>(kb_ + koffs[ks][1])};
+        s[0] = mfma_fp8(a, qf[ks], s[0]);
+      }
+      const bool need_mask = (c0 + BN > w.Lk) || (upper && c0 + BN - 1 > wa + off) ||
+                             (p.window > 0 && c0 < wb + off - p.window + 1);
+      if (need_mask) mask_blocks<1>(s, c0, hl, qrow, off, w.Lk, upper, p.window);
 
-    const bool need_mask = (c0 + kBlockN > w.Lk) || (upper && c0 + kBlockN - 1 > wa + off) ||
-                           (p.window > 0 && c0 < wb + off - p.window + 1);
-    if (need_mask) mask_tile(s, c0, hl, qrow, off, w.Lk, upper, p.window);
+      // optimistic softmax, exactly as in the 16-bit kernel
+      u32x4 pk[2];
+      float part;
+      auto exp_tile = [&](float ref) __attribute__((always_inline)) {
+        float sum0 = 0.0f, sum1 = 0.0f;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int r = 8 * t2;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r + 2 * i], mul, -ref));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r + 2 * i + 1], mul, -ref));
+            sum0 = (t2 == 0 && i == 0) ? p0 : sum0 + p0;
+            sum1 = (t2 == 0 && i == 0) ? p1 : sum1 + p1;
+            pk[t2][i] = pack2<E_BF16>(p0, p1);
+          }
+        }
+        part = sum0 + sum1;
+      };
+      exp_tile(st.m);  // a row's first tile (m = -inf) gives a non-finite sum
+      if (wave_any(!(part <= kPartialSumBound))) {
+        float a = s[0][0], b = s[0][1];
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) {
+          a = __builtin_elementwise_maximum(a, s[0][r]);
+          b = __builtin_elementwise_maximum(b, s[0][r + 1]);
+        }
+        const float mx = swap_halves_max(__builtin_elementwise_maximum(a, b)) * mul;
+        const bool up = mx > st.m;  // -inf stays -inf
+        const float alpha = up ? __builtin_amdgcn_exp2f(st.m - mx) : 1.0f;
+        st.m = up ? mx : st.m;
+        st.l *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::NOB; ++i) st.o[i] *= alpha;
+        exp_tile(st.m == -INFINITY ? 0.0f : st.m);
+      }
+      st.l += part;
 
-    softmax_step8<NOB>(s, st, p.score_mul);
-
-    // P^T operands: step t2 uses registers 8 (t2 % 2) .. +7 of block t2 / 2
-    u32x4 pk[4];
+      // O^T += V^T P^T (bf16)
 #pragma unroll
-    for (int t2 = 0; t2 < 4; ++t2) {
-      const f32x16& sb = s[t2 >> 1];
-      const int r = 8 * (t2 & 1);
+      for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pk[t2][i] = pack2<ELEM>(sb[r + 2 * i], sb[r + 2 * i + 1]);
-    }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int t2 = 0; t2 < 4; ++t2) {
-#pragma unroll
-      for (int db = 0; db < NOB; ++db) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(v_s + (db * 32 + ql) * T::VP + 16 * t2 + 8 * hl);
-        st.o[db] = mfma16<ELEM>(a, pk[t2], st.o[db]);
+        for (int db = 0; db < C::NOB; ++db) {
+          const u32x4 a = vt_operand(vb_ + voffs[db][0] + t2 * 16 * C::VROWB,
+                                     vb_ + voffs[db][1] + t2 * 16 * C::VROWB);
+          st.o[db] = mfma16<E_BF16>(a, pk[t2], st.o[db]);
+        }
       }
     }
+    wait_vm_all();            // K(t+1) DMA and the V(t+1) codes have landed
+    if (more) store_v(vnext, vc);
+    lds_barrier();            // ... for everyone, and V(t+1) is written
+  };
+
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
+    tile(t, lk0, lv0, lk1, lv1);
+    tile(t + 1, lk1, lv1, lk0, lv0);
   }
+  if (t < t1) tile(t, lk0, lv0, lk1, lv1);
 
-  store_row<OUT, D>(p, w, w.h0, qrow, hl, st.m, st.l, st.o);
+  store_row<E_E4M3, D>(p, w, h, qrow, hl, st.m, st.l, st.o);
 }
-
-
 // ---------------------------------------------------------------------------
 // f32 kernel (v_mfma_f32_32x32x2_f32: exact products, f32 accumulation)
 // ---------------------------------------------------------------------------
@@ -1052,7 +1053,7 @@ hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t st
     switch (elem) {
       case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 128, kNkb, kWpe>)); break;
       case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 128, kNkb, kWpe>)); break;
-      case E_E4M3: VLGQA_LAUNCH((fwd8_kernel<E_E4M3, 128>)); break;
+      case E_E4M3: VLGQA_LAUNCH((fwd8_kernel<128>)); break;
       case E_F32: VLGQA_LAUNCH((fwd32_kernel<128>)); break;
       default: return hipErrorInvalidValue;
     }
@@ -1060,7 +1061,7 @@ hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t st
     switch (elem) {
       case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 64, kNkb, kWpe>)); break;
       case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 64, kNkb, kWpe>)); break;
-      case E_E4M3: VLGQA_LAUNCH((fwd8_kernel<E_E4M3, 64>)); break;
+      case E_E4M3: VLGQA_LAUNCH((fwd8_kernel<64>)); break;
       case E_F32: VLGQA_LAUNCH((fwd32_kernel<64>)); break;
       default: return hipErrorInvalidValue;
     }
