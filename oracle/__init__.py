@@ -25,6 +25,8 @@ Modules:
   brute      -- pure-Python triple loop with math.fsum, for tiny inputs.
   online     -- the tiled online-softmax recurrence (realizar IMP-111b) in f64.
   e4m3       -- OCP FP8 E4M3 ("fn") decode and round-to-nearest-even encode.
+  backward   -- the gradient of the forward definition (dq, dk, dv), summed
+                over the query heads of a GQA group for dk/dv.
 
 Parity pins for every function live in ``tests/test_oracle_pins.py``; none of
 them compares the oracle with itself.
@@ -41,4 +43,5 @@ from .attention import (  # noqa: F401
     dense_rows,
     fp8_rows,
 )
+from .backward import attend_rows_bwd, varlen_attention_bwd, flash_attention_bwd  # noqa: F401
 from . import brute, online, e4m3  # noqa: F401
