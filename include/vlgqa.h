@@ -1,9 +1,10 @@
 /*
- * vlgqa.h -- C ABI of the MI355X (gfx950) attention forward library.
+ * vlgqa.h -- C ABI of the MI355X (gfx950) attention library.
  *
- * Three entry points: the packed variable-length forward, the dense forward
- * with a KV-capacity stride and sliding window, and the FP8 dense forward.
- * Each computes, for every query row i of every (sequence, query head h):
+ * Forward entry points: the packed variable-length forward, the dense forward
+ * with a KV-capacity stride and sliding window, and the FP8 dense forward; and
+ * the packed and dense backward passes (declared further down).  The
+ * forwards compute, for every query row i of every (sequence, query head h):
  *
  *     kv_head = h / (num_heads / num_kv_heads)              (GQA, no repeat)
  *     s_j     = scale * <q_i, k_j>,   scale = 1/sqrt(head_dim)
@@ -129,6 +130,74 @@ int flash_attention_fwd_fp8(const void* q, const void* k, const void* v,
                             int64_t seqlen_q, int64_t seqlen_k, int64_t head_dim,
                             int causal, float q_scale, float k_scale, float v_scale,
                             float o_scale, void* out, float* lse, void* hip_stream);
+
+/*
+ * Backward passes.  Gradients of the forward above for a loss whose gradient
+ * with respect to O is dout:
+ *
+ *     P_ij  = exp(scale q_i.k_j - LSE_i)          (visible pairs; recomputed)
+ *     dv_j  = sum_i P_ij dout_i,   dS_ij = P_ij (dout_i.v_j - delta_i),
+ *     delta_i = dout_i.out_i,      dq_i = scale sum_j dS_ij k_j,
+ *     dk_j  = scale sum_i dS_ij q_i,
+ *
+ * with dk and dv of a kv head summed over the num_heads / num_kv_heads query
+ * heads that share it.  out and lse are the forward's results for the same
+ * inputs (lse natural log, -inf for a row with no visible key).  The masks
+ * are those of the forward.  dtype: VLGQA_BF16 or VLGQA_F16 (f32 and FP8 are
+ * not compiled: EUNSUPPORTED); f32 accumulation, gradients stored in dtype.
+ *
+ * workspace: caller-allocated float32 scratch of 2 * (rows * num_heads)
+ * floats, rows = total_q (packed) or batch * seqlen_q (dense), 16-byte
+ * aligned.  On return it holds LSE * log2(e) (+inf for rows with no visible
+ * key) and then delta, head-major ([num_heads][total_q], dense
+ * [batch][num_heads][seqlen_q]).  Calls that share a workspace on one stream
+ * are ordered by the stream; concurrent calls need separate workspaces.
+ * dq, dk, dv are written in full (zero for rows / keys that take part in no
+ * visible pair); padding outside the sequences is not written.
+ */
+
+/*
+ * Packed variable-length backward.
+ * boostr 0.2.0, src/ops/traits/attention/varlen_attention.rs,
+ * VarLenAttentionOps::varlen_attention_bwd (full GQA: dk, dv shaped like k, v;
+ * returns dq, dk, dv).
+ *
+ *   dout, out, q, dq  [total_q, num_heads, head_dim]      dtype
+ *   k, v, dk, dv      [total_k, num_kv_heads, head_dim]   dtype
+ *   lse               [total_q, num_heads]                float32
+ *   cu_seqlens_q/k, max_seqlen_q/k, causal: as in varlen_attention_fwd.
+ *
+ * Errors: as varlen_attention_fwd, plus EUNSUPPORTED for a dtype other than
+ * VLGQA_BF16 / VLGQA_F16.
+ */
+int varlen_attention_bwd(const void* dout, const void* q, const void* k, const void* v,
+                         const void* out, const float* lse,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int64_t total_q, int64_t total_k, int64_t batch_size,
+                         int64_t num_heads, int64_t num_kv_heads,
+                         int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t head_dim,
+                         int causal, int dtype, void* dq, void* dk, void* dv,
+                         float* workspace, void* hip_stream);
+
+/*
+ * Dense backward.  boostr, src/ops/traits/attention/flash.rs,
+ * FlashAttentionOps::flash_attention_bwd (gradients with the shapes of the
+ * inputs; causal and sliding window as in the forward).  The method takes no
+ * kv_seq_len: all seqlen_k keys of k and v are attended.
+ *
+ *   dout, out, q, dq  [batch, num_heads, seqlen_q, head_dim]     dtype
+ *   k, v, dk, dv      [batch, num_kv_heads, seqlen_k, head_dim]  dtype
+ *   lse               [batch, num_heads, seqlen_q]               float32
+ *
+ * Errors: as flash_attention_fwd, plus EUNSUPPORTED for a dtype other than
+ * VLGQA_BF16 / VLGQA_F16.
+ */
+int flash_attention_bwd(const void* dout, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse,
+                        int64_t batch, int64_t num_heads, int64_t num_kv_heads,
+                        int64_t seqlen_q, int64_t seqlen_k, int64_t head_dim,
+                        int causal, int64_t window_size, int dtype,
+                        void* dq, void* dk, void* dv, float* workspace, void* hip_stream);
 
 /* "argument: reason" for the last non-OK return on this thread ("" if none). */
 const char* vlgqa_last_error(void);

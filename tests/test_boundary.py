@@ -34,10 +34,11 @@ def err(lib):
     return lib.vlgqa_last_error().decode()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("varlen_attention_fwd", "flash_attention_fwd", "flash_attention_fwd_fp8",
-              "vlgqa_last_error", "vlgqa_version"):
+              "varlen_attention_bwd", "flash_attention_bwd", "vlgqa_last_error",
+              "vlgqa_version"):
         assert n in names
 
 
@@ -158,3 +159,76 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+# --------------------------------------------------------------------------
+# backward entry points
+# --------------------------------------------------------------------------
+
+def varlen_bwd(lib, **kw):
+    a = dict(do=A, q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, tq=940, tk=940, b=3, h=4, hkv=2,
+             mq=512, mk=512, d=128, causal=1, dtype=BF16, dq=A, dk=A, dv=A, ws=A)
+    a.update(kw)
+    return lib.varlen_attention_bwd(a["do"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"],
+                                    a["ck"], a["tq"], a["tk"], a["b"], a["h"], a["hkv"], a["mq"],
+                                    a["mk"], a["d"], a["causal"], a["dtype"], a["dq"], a["dk"],
+                                    a["dv"], a["ws"], None)
+
+
+def dense_bwd(lib, **kw):
+    a = dict(do=A, q=A, k=A, v=A, o=A, lse=A, b=2, h=8, hkv=2, sq=300, sk=300, d=64, causal=1,
+             w=0, dtype=BF16, dq=A, dk=A, dv=A, ws=A)
+    a.update(kw)
+    return lib.flash_attention_bwd(a["do"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["b"],
+                                   a["h"], a["hkv"], a["sq"], a["sk"], a["d"], a["causal"],
+                                   a["w"], a["dtype"], a["dq"], a["dk"], a["dv"], a["ws"], None)
+
+
+@pytest.mark.parametrize("kw,code,arg", [
+    (dict(dtype=F32), EUNSUP, "dtype"),
+    (dict(dtype=9), EUNSUP, "dtype"),
+    (dict(d=96), EUNSUP, "head_dim"),
+    (dict(h=6, hkv=4), EINVAL, "num_heads"),
+    (dict(tk=-1), EINVAL, "total_k"),
+    (dict(mk=-1), EINVAL, "max_seqlen_k"),
+    (dict(causal=3), EINVAL, "causal"),
+    (dict(cq=0), EINVAL, "cu_seqlens_q"),
+    (dict(k=MIS), EINVAL, "k"),
+    (dict(dk=0), EINVAL, "dk"),
+    (dict(dv=MIS), EINVAL, "dv"),
+    (dict(do=0), EINVAL, "dout"),
+    (dict(o=MIS), EINVAL, "out"),
+    (dict(lse=0), EINVAL, "lse"),
+    (dict(dq=MIS), EINVAL, "dq"),
+    (dict(ws=0), EINVAL, "workspace"),
+    (dict(ws=MIS), EINVAL, "workspace"),
+])
+def test_varlen_bwd_rejects(lib, kw, code, arg):
+    assert varlen_bwd(lib, **kw) == code
+    assert err(lib).startswith(arg + ":"), err(lib)
+
+
+@pytest.mark.parametrize("kw,code,arg", [
+    (dict(dtype=F32), EUNSUP, "dtype"),
+    (dict(d=32), EUNSUP, "head_dim"),
+    (dict(w=-1), EINVAL, "window_size"),
+    (dict(sk=-1), EINVAL, "seqlen_k"),
+    (dict(b=-1), EINVAL, "batch"),
+    (dict(h=8, hkv=3), EINVAL, "num_heads"),
+    (dict(v=0), EINVAL, "v"),
+    (dict(q=MIS), EINVAL, "q"),
+    (dict(ws=MIS), EINVAL, "workspace"),
+])
+def test_dense_bwd_rejects(lib, kw, code, arg):
+    assert dense_bwd(lib, **kw) == code
+    assert err(lib).startswith(arg + ":"), err(lib)
+
+
+def test_bwd_empty_problems_return_ok_without_pointers(lib):
+    none = dict(do=0, q=0, k=0, v=0, o=0, lse=0, cq=0, ck=0, dq=0, dk=0, dv=0, ws=0)
+    assert varlen_bwd(lib, b=0, **none) == _lib.VLGQA_OK
+    assert varlen_bwd(lib, tq=0, tk=0, **none) == _lib.VLGQA_OK
+    none.pop("cq"), none.pop("ck")
+    assert dense_bwd(lib, b=0, **none) == _lib.VLGQA_OK
+    assert dense_bwd(lib, sq=0, sk=0, **none) == _lib.VLGQA_OK
+    assert err(lib) == ""

@@ -1,15 +1,20 @@
-"""MI355X-native fused attention forward over packed variable-length sequences.
+"""MI355X-native fused attention over packed variable-length sequences.
 
 Entry points (HIP kernels for gfx950 behind a C ABI, see include/vlgqa.h):
   varlen_attention_fwd     packed [total, H, D] with I32 cu_seqlens, GQA, causal
   flash_attention_fwd      dense [B, H, S, D], KV capacity stride, sliding window
   flash_attention_fwd_fp8  dense OCP E4M3 with per-tensor scales
-Each returns (output, logsumexp).
+      -> (output, logsumexp)
+  varlen_attention_bwd     gradients of the packed forward
+  flash_attention_bwd      gradients of the dense forward
+      -> (dq, dk, dv)
 """
 
 from .attention import (  # noqa: F401
+    flash_attention_bwd,
     flash_attention_fwd,
     flash_attention_fwd_fp8,
+    varlen_attention_bwd,
     varlen_attention_fwd,
 )
 from ._lib import VlgqaError  # noqa: F401

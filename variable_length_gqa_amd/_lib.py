@@ -22,6 +22,8 @@ SIGNATURES = {
                                  _I, _P, _P, _P]),
     "flash_attention_fwd_fp8": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I, _F, _F,
                                      _F, _F, _P, _P, _P]),
+    "varlen_attention_bwd": (_I, [_P] * 8 + [_I64] * 8 + [_I, _I] + [_P] * 5),
+    "flash_attention_bwd": (_I, [_P] * 6 + [_I64] * 6 + [_I, _I64, _I] + [_P] * 5),
     "vlgqa_last_error": (ctypes.c_char_p, []),
     "vlgqa_version": (ctypes.c_char_p, []),
 }

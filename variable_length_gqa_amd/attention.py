@@ -9,7 +9,9 @@ Argument order follows the pages' signatures:
     ``VarLenAttentionOps::varlen_attention_fwd``
   * boostr, src/ops/traits/attention/flash.rs,
     ``FlashAttentionOps::flash_attention_fwd`` / ``flash_attention_fwd_fp8``
-All return ``(output, logsumexp)``.
+The forwards return ``(output, logsumexp)``; the backwards
+(``VarLenAttentionOps::varlen_attention_bwd``,
+``FlashAttentionOps::flash_attention_bwd``) return ``(dq, dk, dv)``.
 """
 
 from __future__ import annotations
@@ -177,3 +179,84 @@ def flash_attention_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n
                                      _ptr(lse), _stream(dev))
     _lib.check(rc)
     return out, lse
+
+
+_BWD_DTYPES = (torch.bfloat16, torch.float16)
+
+
+def _check_bwd_common(dout, q, k, v, out, lse, dev):
+    for name, t in (("dout", dout), ("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse)):
+        _check_device_tensor(name, t, dev)
+    _need(q.dtype in _BWD_DTYPES, f"the backward supports bf16 and f16, not {q.dtype}")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype and dout.dtype == q.dtype
+          and out.dtype == q.dtype, "dout, q, k, v and out must share one dtype")
+    _need(dout.shape == q.shape and out.shape == q.shape, "dout and out must have the shape of q")
+    _need(v.shape == k.shape, "v must have the shape of k")
+    _need(lse.dtype == torch.float32, "lse must be float32")
+
+
+def varlen_attention_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         output: torch.Tensor, lse: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                         cu_seqlens_k: torch.Tensor, batch_size: int, num_heads: int,
+                         num_kv_heads: int, max_seqlen_q: int, max_seqlen_k: int, head_dim: int,
+                         causal: bool, check_seqlens: bool | None = None):
+    """Packed variable-length attention backward -> (dq [total_q,H,D], dk, dv [total_k,Hkv,D]).
+
+    ``output`` and ``lse`` are the forward's results for the same inputs.
+    """
+    dev = q.device
+    _check_bwd_common(dout, q, k, v, output, lse, dev)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        _check_device_tensor(name, t, dev)
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32,
+          "cu_seqlens must be int32")
+    _need(q.dim() == 3 and q.shape[1] == num_heads and q.shape[2] == head_dim,
+          "q must be [total_q, num_heads, head_dim]")
+    _need(k.dim() == 3 and k.shape[1] == num_kv_heads and k.shape[2] == head_dim,
+          "k must be [total_k, num_kv_heads, head_dim]")
+    _need(cu_seqlens_q.numel() == batch_size + 1 and cu_seqlens_k.numel() == batch_size + 1,
+          "cu_seqlens must have batch_size + 1 entries")
+    total_q, total_k = q.shape[0], k.shape[0]
+    _need(lse.shape == (total_q, num_heads), "lse must be [total_q, num_heads]")
+    if check_seqlens if check_seqlens is not None else DEBUG_CHECKS:
+        check_cu_seqlens(cu_seqlens_q, total_q, max_seqlen_q, "cu_seqlens_q")
+        check_cu_seqlens(cu_seqlens_k, total_k, max_seqlen_k, "cu_seqlens_k")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((2 * max(total_q, 1) * num_heads,), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    rc = lib.varlen_attention_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(output), _ptr(lse),
+                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), total_q, total_k,
+                                  batch_size, num_heads, num_kv_heads, max_seqlen_q,
+                                  max_seqlen_k, head_dim, int(bool(causal)),
+                                  _DTYPE_CODE[q.dtype], _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                  _stream(dev))
+    _lib.check(rc)
+    return dq, dk, dv
+
+
+def flash_attention_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        output: torch.Tensor, lse: torch.Tensor, num_heads: int,
+                        num_kv_heads: int, head_dim: int, causal: bool, window_size: int = 0):
+    """Dense attention backward -> (dq [B,H,S_q,D], dk, dv [B,Hkv,S_k,D]).
+
+    All S_k keys of k/v are attended (the pages' backward takes no kv_seq_len).
+    """
+    dev = q.device
+    _check_bwd_common(dout, q, k, v, output, lse, dev)
+    _need(q.dim() == 4 and q.shape[1] == num_heads and q.shape[3] == head_dim,
+          "q must be [B, num_heads, S_q, head_dim]")
+    _need(k.dim() == 4 and k.shape[0] == q.shape[0] and k.shape[1] == num_kv_heads
+          and k.shape[3] == head_dim, "k must be [B, num_kv_heads, S_k, head_dim]")
+    _need(window_size >= 0, "window_size must be non-negative")
+    B, _, Sq, _ = q.shape
+    Sk = k.shape[2]
+    _need(lse.shape == (B, num_heads, Sq), "lse must be [B, num_heads, S_q]")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((2 * max(B * Sq, 1) * num_heads,), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    rc = lib.flash_attention_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(output), _ptr(lse),
+                                 B, num_heads, num_kv_heads, Sq, Sk, head_dim,
+                                 int(bool(causal)), int(window_size), _DTYPE_CODE[q.dtype],
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), _stream(dev))
+    _lib.check(rc)
+    return dq, dk, dv

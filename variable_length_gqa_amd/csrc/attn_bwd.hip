@@ -1,0 +1,575 @@
+// Fused attention backward for gfx950 (CDNA4): packed varlen and dense layouts,
+// GQA, causal / sliding-window masks, bf16 / f16 storage, f32 accumulation.
+//
+// What is computed (the gradient of the forward, for the interface of boostr
+// varlen_attention.rs ``varlen_attention_bwd`` and boostr flash.rs
+// ``flash_attention_bwd``: dout, q, k, v, the forward output and its
+// logsumexp in, dq / dk / dv out, dk and dv shaped like k and v under GQA):
+//   P_ij  = exp(scale q_i.k_j - LSE_i)            (recomputed from the LSE)
+//   dv_j  = sum_i P_ij dO_i
+//   dS_ij = P_ij (dO_i.v_j - delta_i),   delta_i = dO_i.O_i
+//   dq_i  = scale sum_j dS_ij k_j,       dk_j = scale sum_i dS_ij q_i
+// with dk / dv of a kv head summed over its G query heads.
+//
+// Three launches:
+//   bwd_rowsum_kernel  delta_i = dO_i.O_i and LSE_i log2(e) per (row, head),
+//                      written head-major into the caller's workspace (so a
+//                      query tile's values are contiguous).
+//   bwd_dkdv_kernel    one workgroup per (sequence, kv head, 128-key tile),
+//                      4 waves x 32 keys; K and V of the wave's keys stay in
+//                      registers; the loop runs over the G query heads and the
+//                      32-row query tiles that see the keys, with Q, dO and the
+//                      tile's LSE / delta brought to LDS by DMA (double
+//                      buffered).  dK and dV accumulate in registers: no atomics,
+//                      deterministic.
+//   bwd_dq_kernel      one workgroup per (sequence, 128-row query tile, query
+//                      head), the forward's structure: K/V tiles of 32 keys by
+//                      DMA into LDS, Q^T and dO^T in registers, dQ^T in
+//                      registers.
+// Matrix-core formulation (v_mfma_f32_32x32x16_{bf16,f16}): every product has
+// the operand layouts of the forward kernel.  In dK/dV the lane owns a key:
+//   S  = Q K^T     A = Q rows (LDS), B = K^T (registers)  -> lane: key l % 32,
+//   dP = dO V^T    A = dO rows (LDS), B = V^T (registers)    16 query rows
+//   dV^T += dO^T P     A = dO^T by transposing LDS reads, B = P (bf16)
+//   dK^T += Q^T dS     A = Q^T by transposing LDS reads,  B = dS (bf16)
+// In dQ the lane owns a query:
+//   S^T = K Q^T, dP^T = V dO^T   A = K / V rows (LDS), B = Q^T / dO^T (registers)
+//   dQ^T += K^T dS^T             A = K^T by transposing LDS reads, B = dS^T
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bwd_params.h"
+#include "kernel_common.h"
+
+namespace vlgqa {
+
+constexpr int kTileB = 128;  // keys per dK/dV workgroup, query rows per dQ workgroup
+
+template <int ELEM>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (ELEM == E_F16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  } else {
+    return __uint_as_float(w << 16);
+  }
+}
+template <int ELEM>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (ELEM == E_F16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  } else {
+    return __uint_as_float(w & 0xFFFF0000u);
+  }
+}
+
+// Workspace layout (f32): [2][B][H][rows]: plane 0 = LSE * log2(e) (+inf for a
+// row with no visible key, so its weights are exp2(-inf) = 0), plane 1 = delta.
+// Dense: rows = S_q per batch; packed: B = 1 and rows = total_q.
+__device__ __forceinline__ int64_t ws_index(const BwdParams& p, int b, int64_t r, int h) {
+  return ((int64_t)b * p.heads + h) * p.d_rows + r;
+}
+__device__ __forceinline__ int64_t ws_plane(const BwdParams& p) {
+  return (int64_t)p.d_batch * p.heads * p.d_rows;
+}
+
+// ---------------------------------------------------------------------------
+// delta and the log2-domain LSE
+// ---------------------------------------------------------------------------
+//
+// D/8 lanes per (row, head), 16 bytes of dO and of O each, reduced across
+// those lanes; rows are (b, r, h) with h fastest, so a wave reads contiguous
+// memory in both layouts.
+template <int ELEM, int D>
+__global__ __launch_bounds__(256) void bwd_rowsum_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int PPW = 64 / LPR;
+  const int64_t npairs = (int64_t)p.d_batch * p.d_rows * p.heads;
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * PPW + lane / LPR;
+  const int sub = lane % LPR;
+  float acc = 0.0f;
+  int h = 0, b = 0;
+  int64_t r = 0;
+  if (pair < npairs) {
+    h = (int)(pair % p.heads);
+    const int64_t rest = pair / p.heads;
+    r = rest % p.d_rows;
+    b = (int)(rest / p.d_rows);
+    const int64_t off = (int64_t)b * p.q_bs + r * p.q_rs + (int64_t)h * p.q_hs + sub * 8;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.dout) + off);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.o) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc += lo16<ELEM>(a[i]) * lo16<ELEM>(c[i]) + hi16<ELEM>(a[i]) * hi16<ELEM>(c[i]);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (pair < npairs && sub == 0) {
+    const float lse = p.lse[(int64_t)b * p.l_bs + r * p.l_rs + (int64_t)h * p.l_hs];
+    const int64_t wi = ws_index(p, b, r, h);
+    p.delta[wi] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    p.delta[ws_plane(p) + wi] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// shared pieces
+// ---------------------------------------------------------------------------
+
+struct SeqBounds {
+  int q_start, Lq, k_start, Lk;
+};
+
+__device__ __forceinline__ SeqBounds seq_bounds(const BwdParams& p, int b) {
+  SeqBounds s{0, p.seqlen_q, 0, p.seqlen_k};
+  if (p.cu_q) {
+    s.q_start = p.cu_q[b];
+    s.Lq = p.cu_q[b + 1] - s.q_start;
+  }
+  if (p.cu_k) {
+    s.k_start = p.cu_k[b];
+    s.Lk = p.cu_k[b + 1] - s.k_start;
+  }
+  return s;
+}
+
+// the 16-bit tile layout of the forward kernel: 32 rows of D elements, rows
+// unpadded, 16-byte chunks XOR-swizzled by swz<D>(row)
+template <int D>
+struct T16 {
+  static constexpr int ROWB = 2 * D;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int TILE = 32 * ROWB;
+  static constexpr int CPT = TILE / 16 / kThreads;   // DMA chunks per thread
+  static constexpr int NS = D / 16;
+  static constexpr int NOB = D / 32;
+  static_assert(CPT >= 1 && (TILE / 16) % kThreads == 0, "tile shape");
+};
+
+// per-thread DMA offsets of a 32-row tile whose rows are rs bytes apart
+template <int D>
+__device__ __forceinline__ void tile_dma_offsets(uint32_t (&voff)[T16<D>::CPT], int wid, int lane,
+                                                 uint32_t rs) {
+  using C = T16<D>;
+#pragma unroll
+  for (int n = 0; n < C::CPT; ++n) {
+    const int P = (wid * C::CPT + n) * 64 + lane;
+    const int row = P / C::CPR, ch = (P % C::CPR) ^ swz<D>(row);
+    voff[n] = (uint32_t)row * rs + ch * 16;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dma_tile16(const uint8_t* buf, u32x4 rsrc, uint32_t base, int wid,
+                                           const uint32_t (&voff)[T16<D>::CPT]) {
+  using C = T16<D>;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)buf;
+#pragma unroll
+  for (int n = 0; n < C::CPT; ++n) dma16(lds0 + (wid * C::CPT + n) * 1024, base + voff[n], rsrc);
+}
+
+// row-operand read offset of lane (row ql, half hl) for k-step 0: the
+// offset of step ks is this ^ (ks << 5) (as in the forward)
+template <int D>
+__device__ __forceinline__ uint32_t row_read_off(int ql, int hl) {
+  return (uint32_t)ql * T16<D>::ROWB + (uint32_t)((hl ^ swz<D>(ql)) * 16);
+}
+
+// transposing-read offsets (the forward's V^T operand)
+template <int D>
+__device__ __forceinline__ void tr_read_offsets(uint32_t (&o)[T16<D>::NOB][2], int lane) {
+  const int g = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
+#pragma unroll
+  for (int db = 0; db < T16<D>::NOB; ++db)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 8 * c + 4 * (g >> 1) + e;
+      const int ch = 4 * db + 2 * (g & 1) + (j >> 1);
+      o[db][c] = (uint32_t)row * T16<D>::ROWB + (uint32_t)((ch ^ swz<D>(row)) * 16) + (j & 1) * 8;
+    }
+}
+
+// store a [key or query][d] row block held as 32-row accumulators (lane: row
+// l % 32, d = 32 db + 8 (r / 4) + 4 (l / 32) + r % 4), times mul
+template <int ELEM, int D>
+__device__ __forceinline__ void store_rows(void* base, int64_t row_off, int hl,
+                                           const f32x16 (&acc)[D / 32], float mul) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + g * 8 + 4 * hl;
+      const u32x2 v = {pack2<ELEM>(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul),
+                       pack2<ELEM>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + row_off + d0) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV
+// ---------------------------------------------------------------------------
+
+template <int ELEM, int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+  using C = T16<D>;
+  // stage buffer: Q tile, dO tile, then 32 lse2 + 32 delta floats
+  constexpr int STAGE = 2 * C::TILE + 256;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+
+  const int BK = p.batch * p.kv_heads;
+  const int grp = blockIdx.x;
+  const int kt = grp / BK;
+  const int b = (grp % BK) / p.kv_heads;
+  const int kvh = grp % p.kv_heads;
+  const SeqBounds sb = seq_bounds(p, b);
+  const int k0 = kt * kTileB;
+  if (k0 >= sb.Lk) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ql = lane & 31;
+  const int kw = k0 + 32 * wid;           // the wave's first key
+  const int key = kw + ql;                // this lane's key
+  const int off = sb.Lk - sb.Lq;
+  const bool upper = p.causal || p.window > 0;
+  const float mul = p.score_mul;
+
+  // K^T / V^T fragments of the lane's key: k[key][16 ks + 8 hl .. +8]
+  u32x4 kf[C::NS], vf[C::NS];
+  {
+    const int64_t koff = ((int64_t)b * p.k_bs + (int64_t)sb.k_start * p.k_rs +
+                          (int64_t)kvh * p.k_hs) * 2;
+    const uint32_t bytes = sat_bytes((int64_t)sb.Lk * p.k_rs * 2);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
+    const uint32_t roff = (uint32_t)key * (uint32_t)(p.k_rs * 2);
+#pragma unroll
+    for (int ks = 0; ks < C::NS; ++ks) {
+      kf[ks] = bload16(kr, roff + (16 * ks + 8 * hl) * 2);
+      vf[ks] = bload16(vr, roff + (16 * ks + 8 * hl) * 2);
+    }
+  }
+  f32x16 dk[C::NOB], dv[C::NOB];
+#pragma unroll
+  for (int i = 0; i < C::NOB; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  // query rows that see any key of the workgroup / of this wave
+  const int k1 = min(k0 + kTileB, sb.Lk);
+  const int qa = upper ? max(0, k0 - off) : 0;
+  const int qb = p.window > 0 ? min(sb.Lq, k1 - 1 - off + p.window) : sb.Lq;
+  const int ta = qa / 32, tb = qb > qa ? (qb + 31) / 32 : ta;
+  const int nt = tb - ta;
+  const int nst = nt * p.group;  // stages: (query head, query tile)
+  const int kw1 = min(kw + 32, sb.Lk);
+  const bool wave_keys = kw < sb.Lk;
+  const int wqa = upper ? max(0, kw - off) : 0;
+  const int wqb = p.window > 0 ? min(sb.Lq, kw1 - 1 - off + p.window) : sb.Lq;
+
+  uint32_t voff[C::CPT];
+  tile_dma_offsets<D>(voff, wid, lane, (uint32_t)(p.q_rs * 2));
+  const uint32_t roff0 = row_read_off<D>(ql, hl);
+  uint32_t troff[C::NOB][2];
+  tr_read_offsets<D>(troff, lane);
+  const int64_t plane = ws_plane(p);
+
+  // DMA of stage s into buffer u: Q and dO tiles of (head, tile), lse2/delta
+  auto issue = [&](int s, int u) __attribute__((always_inline)) {
+    const int hh = s / nt, t = ta + s % nt;
+    const int h = kvh * p.group + hh;
+    const int64_t qoff = ((int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs +
+                          (int64_t)h * p.q_hs) * 2;
+    const uint32_t bytes = sat_bytes((int64_t)sb.Lq * p.q_rs * 2);
+    const uint32_t base = (uint32_t)(t * 32) * (uint32_t)(p.q_rs * 2);
+    const uint8_t* buf = lds + u * STAGE;
+    dma_tile16<D>(buf, rsrc_words(reinterpret_cast<const uint8_t*>(p.q) + qoff, bytes), base,
+                  wid, voff);
+    dma_tile16<D>(buf + C::TILE, rsrc_words(reinterpret_cast<const uint8_t*>(p.dout) + qoff, bytes),
+                  base, wid, voff);
+    if (wid < 2 && lane < 8) {
+      // wave 0: lse2 of rows 32 t .. +32 (4 per lane), wave 1: delta; rows past
+      // the sequence arrive as zeros
+      const int64_t wi = ws_index(p, p.cu_q ? 0 : b, p.cu_q ? (int64_t)sb.q_start : 0, h);
+      const float* src = p.delta + wi + (wid == 1 ? plane : 0);
+      dma16((uint32_t)(uintptr_t)(lds_void*)(buf + 2 * C::TILE + wid * 128),
+            (uint32_t)(t * 32 * 4 + lane * 16), rsrc_words(src, sat_bytes((int64_t)sb.Lq * 4)));
+    }
+  };
+
+  if (nst > 0) issue(0, 0);
+  wait_vm_all();
+  lds_barrier();
+
+  for (int s = 0; s < nst; ++s) {
+    const int u = s & 1;
+    if (s + 1 < nst) issue(s + 1, u ^ 1);
+    const int t = ta + s % nt;
+    const int q0 = t * 32;
+    if (wave_keys && q0 < wqb && q0 + 32 > wqa) {
+      const uint8_t* qt = lds + u * STAGE;
+      const uint8_t* dot = qt + C::TILE;
+      const float* wsv = reinterpret_cast<const float*>(qt + 2 * C::TILE);
+      f32x16 sc = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < C::NS; ++ks) {
+        const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
+        sc = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(qt + ro), kf[ks], sc);
+        dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(dot + ro), vf[ks], dp);
+      }
+      // register r holds query row q0 + qq(r) + 4 hl, qq(r) = 8 (r / 4) + r % 4
+      f32x4 l2[4], dl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l2[j] = *reinterpret_cast<const f32x4*>(wsv + 8 * j + 4 * hl);
+        dl[j] = *reinterpret_cast<const f32x4*>(wsv + 32 + 8 * j + 4 * hl);
+      }
+      const bool need_mask = key >= sb.Lk || q0 + 32 > sb.Lq ||
+                             (upper && kw + 31 > q0 + off) ||
+                             (p.window > 0 && kw < q0 + 31 + off - p.window + 1);
+      if (need_mask) {
+        // visible iff key <= q + off (causal), key >= q + off - W + 1 (window),
+        // q < Lq, key < Lk; with q = q0 + 4 hl + qq:
+        const int base = q0 + 4 * hl;
+        const int lo = upper ? key - off - base : INT32_MIN / 2;       // qq >= lo
+        const int hi = min(sb.Lq - 1 - base,
+                           p.window > 0 ? key - off + p.window - 1 - base : INT32_MAX / 2);
+        const bool kin = key < sb.Lk;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qq = 8 * (r >> 2) + (r & 3);
+          if (!kin || qq < lo || qq > hi) sc[r] = -INFINITY;
+        }
+      }
+      u32x4 pk[2], dsk[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * t2 + 2 * i;
+          const int j = r >> 2, e = r & 3;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], mul, -l2[j][e]));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r + 1], mul, -l2[j][e + 1]));
+          pk[t2][i] = pack2<ELEM>(p0, p1);
+          dsk[t2][i] = pack2<ELEM>(p0 * (dp[r] - dl[j][e]), p1 * (dp[r + 1] - dl[j][e + 1]));
+        }
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+        for (int db = 0; db < C::NOB; ++db) {
+          const uint32_t o0 = troff[db][0] + t2 * 16 * C::ROWB, o1 = troff[db][1] + t2 * 16 * C::ROWB;
+          dv[db] = mfma16<ELEM>(vt_operand(dot + o0, dot + o1), pk[t2], dv[db]);
+          dk[db] = mfma16<ELEM>(vt_operand(qt + o0, qt + o1), dsk[t2], dk[db]);
+        }
+      }
+    }
+    wait_vm_all();
+    lds_barrier();
+  }
+
+  if (key < sb.Lk) {
+    const int64_t row = (int64_t)b * p.k_bs + (int64_t)(sb.k_start + key) * p.k_rs +
+                        (int64_t)kvh * p.k_hs;
+    store_rows<ELEM, D>(p.dk, row, hl, dk, p.scale);
+    store_rows<ELEM, D>(p.dv, row, hl, dv, 1.0f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+
+template <int ELEM, int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+  using C = T16<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv1[C::TILE];
+
+  // work: (query tile descending, batch, head); heads of a kv group adjacent
+  const int grp = blockIdx.x;
+  const int h = grp % p.heads;
+  const int b = (grp / p.heads) % p.batch;
+  const int tq = p.n_qtiles - 1 - grp / (p.heads * p.batch);
+  const SeqBounds sb = seq_bounds(p, b);
+  const int r0 = tq * kTileB;
+  if (r0 >= sb.Lq) return;
+  const int kvh = h / p.group;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ql = lane & 31;
+  const int qrow = r0 + 32 * wid + ql;
+  const float mul = p.score_mul;
+  const int off = sb.Lk - sb.Lq;
+  const bool upper = p.causal || p.window > 0;
+
+  // Q^T and dO^T fragments of the lane's row, and its lse2 / delta
+  u32x4 qf[C::NS], of[C::NS];
+  {
+    const int64_t qoff = ((int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs +
+                          (int64_t)h * p.q_hs) * 2;
+    const uint32_t bytes = sat_bytes((int64_t)sb.Lq * p.q_rs * 2);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(reinterpret_cast<const uint8_t*>(p.q) + qoff, bytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(reinterpret_cast<const uint8_t*>(p.dout) + qoff, bytes);
+    const uint32_t roff = (uint32_t)qrow * (uint32_t)(p.q_rs * 2);
+#pragma unroll
+    for (int ks = 0; ks < C::NS; ++ks) {
+      qf[ks] = bload16(qr, roff + (16 * ks + 8 * hl) * 2);
+      of[ks] = bload16(dr, roff + (16 * ks + 8 * hl) * 2);
+    }
+  }
+  float lse2 = INFINITY, dlt = 0.0f;
+  if (qrow < sb.Lq) {
+    const int64_t wi = ws_index(p, p.cu_q ? 0 : b, p.cu_q ? (int64_t)sb.q_start + qrow : qrow, h);
+    lse2 = p.delta[wi];
+    dlt = p.delta[ws_plane(p) + wi];
+  }
+
+  u32x4 krs, vrs;
+  uint32_t rs;
+  {
+    const int64_t koff = ((int64_t)b * p.k_bs + (int64_t)sb.k_start * p.k_rs +
+                          (int64_t)kvh * p.k_hs) * 2;
+    const uint32_t bytes = sat_bytes((int64_t)sb.Lk * p.k_rs * 2);
+    krs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
+    vrs = rsrc_words(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
+    rs = (uint32_t)(p.k_rs * 2);
+  }
+  uint32_t voff[C::CPT];
+  tile_dma_offsets<D>(voff, wid, lane, rs);
+  const uint32_t roff0 = row_read_off<D>(ql, hl);
+  uint32_t troff[C::NOB][2];
+  tr_read_offsets<D>(troff, lane);
+
+  // key range of the workgroup and of this wave
+  const int qa = r0, qb = min(r0 + kTileB, sb.Lq) - 1;
+  const int kv_hi = upper ? min(sb.Lk, qb + off + 1) : sb.Lk;
+  const int kv_lo = p.window > 0 ? max(0, qa + off - p.window + 1) : 0;
+  const int t0 = kv_lo / 32;
+  const int t1 = kv_hi > kv_lo ? (kv_hi + 31) / 32 : t0;
+  const int wa = r0 + 32 * wid, wb = min(wa + 31, sb.Lq - 1);
+  int whi = 0, wlo = 0;
+  if (wa <= wb) {
+    whi = upper ? min(sb.Lk, wb + off + 1) : sb.Lk;
+    wlo = p.window > 0 ? max(0, wa + off - p.window + 1) : 0;
+  }
+
+  f32x16 dq[C::NOB];
+#pragma unroll
+  for (int i = 0; i < C::NOB; ++i) dq[i] = f32x16{};
+
+  if (t0 < t1) {
+    dma_tile16<D>(lk0, krs, (uint32_t)(t0 * 32) * rs, wid, voff);
+    dma_tile16<D>(lv0, vrs, (uint32_t)(t0 * 32) * rs, wid, voff);
+  }
+  wait_vm_all();
+  lds_barrier();
+
+  auto tile = [&](int t, const uint8_t* kb_, const uint8_t* vb_, const uint8_t* knext,
+                  const uint8_t* vnext) __attribute__((always_inline)) {
+    if (t + 1 < t1) {
+      const uint32_t base = (uint32_t)((t + 1) * 32) * rs;
+      dma_tile16<D>(knext, krs, base, wid, voff);
+      dma_tile16<D>(vnext, vrs, base, wid, voff);
+    }
+    const int c0 = t * 32;
+    if (wa <= wb && c0 < whi && c0 + 32 > wlo) {
+      f32x16 sc = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < C::NS; ++ks) {
+        const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
+        sc = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(kb_ + ro), qf[ks], sc);
+        dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(vb_ + ro), of[ks], dp);
+      }
+      // register r holds key c0 + kk(r) + 4 hl, kk(r) = 8 (r / 4) + r % 4
+      const bool need_mask = (c0 + 32 > sb.Lk) || (upper && c0 + 31 > wa + off) ||
+                             (p.window > 0 && c0 < wb + off - p.window + 1);
+      if (need_mask) {
+        const int base = c0 + 4 * hl;
+        const int a = (upper ? min(sb.Lk - 1, qrow + off) : sb.Lk - 1) - base;
+        const int lo = p.window > 0 ? qrow + off - p.window + 1 - base : INT32_MIN / 2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + (r & 3);
+          if (kk > a || kk < lo) sc[r] = -INFINITY;
+        }
+      }
+      u32x4 dsk[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * t2 + 2 * i;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], mul, -lse2));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r + 1], mul, -lse2));
+          dsk[t2][i] = pack2<ELEM>(p0 * (dp[r] - dlt), p1 * (dp[r + 1] - dlt));
+        }
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+        for (int db = 0; db < C::NOB; ++db) {
+          const uint32_t o0 = troff[db][0] + t2 * 16 * C::ROWB, o1 = troff[db][1] + t2 * 16 * C::ROWB;
+          dq[db] = mfma16<ELEM>(vt_operand(kb_ + o0, kb_ + o1), dsk[t2], dq[db]);
+        }
+      }
+    }
+    wait_vm_all();
+    lds_barrier();
+  };
+
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
+    tile(t, lk0, lv0, lk1, lv1);
+    tile(t + 1, lk1, lv1, lk0, lv0);
+  }
+  if (t < t1) tile(t, lk0, lv0, lk1, lv1);
+
+  if (qrow < sb.Lq) {
+    const int64_t row = (int64_t)b * p.q_bs + (int64_t)(sb.q_start + qrow) * p.q_rs +
+                        (int64_t)h * p.q_hs;
+    store_rows<ELEM, D>(p.dq, row, hl, dq, p.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host planning and launch
+// ---------------------------------------------------------------------------
+
+bool plan_bwd(BwdParams& p, int head_dim) {
+  const int64_t nk = ((int64_t)p.max_seqlen_k + kTileB - 1) / kTileB;
+  const int64_t nq = ((int64_t)p.max_seqlen_q + kTileB - 1) / kTileB;
+  if (nk * p.batch * p.kv_heads > INT32_MAX / 2) return false;
+  if (nq * p.batch * p.heads > INT32_MAX / 2) return false;
+  p.n_ktiles = (int32_t)nk;
+  p.n_qtiles = (int32_t)nq;
+  const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
+  return pairs / (4 * (64 / (head_dim / 8))) < INT32_MAX / 2;
+}
+
+hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t stream) {
+  const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
+  const int ppb = 4 * (64 / (head_dim / 8));
+  const dim3 g0((unsigned)((pairs + ppb - 1) / ppb)), g1((unsigned)(p.n_ktiles * p.batch * p.kv_heads)),
+      g2((unsigned)(p.n_qtiles * p.batch * p.heads)), blk(kThreads);
+#define VLGQA_BWD(E, D)                                                        \
+  do {                                                                         \
+    if (pairs > 0) hipLaunchKernelGGL((bwd_rowsum_kernel<E, D>), g0, blk, 0, stream, p); \
+    if (g1.x > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), g1, blk, 0, stream, p);   \
+    if (g2.x > 0) hipLaunchKernelGGL((bwd_dq_kernel<E, D>), g2, blk, 0, stream, p);     \
+  } while (0)
+  if (head_dim == 128 && elem == E_BF16) VLGQA_BWD(E_BF16, 128);
+  else if (head_dim == 128 && elem == E_F16) VLGQA_BWD(E_F16, 128);
+  else if (head_dim == 64 && elem == E_BF16) VLGQA_BWD(E_BF16, 64);
+  else if (head_dim == 64 && elem == E_F16) VLGQA_BWD(E_F16, 64);
+  else return hipErrorInvalidValue;
+#undef VLGQA_BWD
+  return hipGetLastError();
+}
+
+}  // namespace vlgqa

@@ -10,40 +10,32 @@
 // denominator and running weighted sum, rescaled when the maximum grows.
 //
 // Work decomposition: one workgroup = one (sequence, 128-row query tile, query
-// head); 4 waves x 32 query rows.  K/V tiles of 64 keys are staged through LDS
+// head); 4 waves x 32 query rows.  K/V tiles of 32 keys are staged through LDS
 // (double buffered, one barrier per tile) and shared by the 4 waves.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_{bf16,f16}, wave64):
 //   S^T = K Q^T   A = K tile (32 keys x 16 d, from LDS), B = Q^T (registers)
-//                 -> lane l holds query (l % 32) and 16 of the 32 keys of a
-//                    32-key block, so a row's max / sum is an in-lane
-//                    reduction plus one permlane32 swap.
-//   O^T = V^T P^T A = V^T (32 d x 16 keys, LDS holds V transposed),
-//                 B = P^T taken straight from the S^T accumulator registers
-//                 (converted to 16 bit) -> O^T keeps query (l % 32) per lane,
-//                 so the per-row rescale factor is a per-lane scalar.
+//                 -> lane l holds query (l % 32) and 16 of the tile's 32 keys,
+//                    so a row's max / sum is an in-lane reduction plus one
+//                    permlane32 swap.
+//   O^T = V^T P^T A = V^T (32 d x 16 keys, transposing LDS reads of the
+//                 row-major V tile), B = P^T taken straight from the S^T
+//                 accumulator registers (converted to 16 bit) -> O^T keeps
+//                 query (l % 32) per lane, so the per-row rescale factor is a
+//                 per-lane scalar.
 // The P registers cover keys {0-3, 8-11} (lanes 0-31) and {4-7, 12-15}
-// (lanes 32-63) of each 16-key step; V^T is written to LDS with the middle two
-// 4-key quads of every 16 keys swapped so that each lane reads its 8 keys as
-// one 16-byte vector.
+// (lanes 32-63) of each 16-key step; the transposing V reads gather the keys
+// in that order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <type_traits>
 
 #include "fwd_params.h"
+#include "kernel_common.h"
 
 namespace vlgqa {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 // a row's reference maximum is only moved when a tile raises it by more than
 // this (log2 units); until then probabilities may reach 2^kRescaleSlack.  The
 // result is exact either way: numerator and denominator use the same reference.
@@ -51,62 +43,6 @@ constexpr float kRescaleSlack = 8.0f;
 // bf16/f16 kernel: a lane's partial sum of probabilities (32 of them) may
 // reach this before the reference maximum is moved (probabilities <= 2^16).
 constexpr float kPartialSumBound = 65536.0f;
-
-// ---------------------------------------------------------------------------
-// small helpers
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float swap_halves_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float swap_halves_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ bool wave_any(bool pred) {
-  return __builtin_amdgcn_ballot_w64(pred) != 0;
-}
-
-template <int ELEM>
-__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (ELEM == E_F16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  } else {  // bf16, and E4M3 widened to bf16
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-}
-
-// two floats -> packed 16-bit pair (round to nearest even), one v_cvt_pk_*
-template <int ELEM>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  const f32x2 v = {lo, hi};
-  if constexpr (ELEM == E_F16) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  }
-}
-
-// four floats -> four OCP E4M3 codes in one register (v_cvt_pk_fp8_f32: round
-// to nearest even).  Callers keep |x| <= 448 (the largest finite code).
-__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
-
-// clamp to the finite E4M3 range (saturating encode: never a NaN code)
-__device__ __forceinline__ float sat448(float x) {
-  return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f);
-}
 
 // ---------------------------------------------------------------------------
 // work decode: XCD-aware, longest query tiles first
@@ -160,19 +96,6 @@ __device__ __forceinline__ void key_range(const FwdParams& p, const Work& w, int
   const bool upper = p.causal || p.window > 0;
   hi = upper ? min(w.Lk, qb + off + 1) : w.Lk;
   lo = p.window > 0 ? max(0, qa + off - p.window + 1) : 0;
-}
-
-// Range-checked loads: a buffer resource covering [base, base + bytes) returns
-// zeros for any access at or beyond `bytes` (rows past a sequence's end).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t sat_bytes(int64_t b) {
-  return b > 0xFFFFFFFFll ? 0xFFFFFFFFu : (b < 0 ? 0u : (uint32_t)b);
 }
 
 // ---------------------------------------------------------------------------
@@ -300,41 +223,6 @@ struct Cfg5 {
   static_assert(CPT >= 1 && (TILE / 16) % kThreads == 0, "tile shape");
 };
 
-// chunk swizzle of an LDS row: physical chunk = logical chunk ^ swz(row)
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);  // 16 chunks per row
-  else return (row >> 1) & 7;                                       // 8 chunks per row
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
-// (lgkmcnt) but lets global loads and LDS DMA stay in flight across it.  A
-// __syncthreads(), and even an LDS-scoped fence, drains every outstanding
-// vector-memory request (DMA writes count as LDS stores).  DMA into LDS is
-// published by an explicit vmcnt wait before this.  The empty asm statements
-// with a memory clobber keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// wait until no vector-memory request of this wave is outstanding
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Raw buffer descriptor words (base, stride 0, byte range, gfx9 flags).
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  u32x4 r = {(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
-  return r;
-}
-
 // Request one tile (rows c0 .. c0+63) of K or V into an LDS tile buffer: this
 // thread's chunk n goes to LDS chunk (wid*CPT + n)*64 + lane, from tile offset
 // voff[n].  The instruction writes LDS only (no register results).
@@ -345,24 +233,8 @@ __device__ __forceinline__ void dma_tile(uint8_t* buf, u32x4 rsrc, uint32_t base
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)buf;
 #pragma unroll
   for (int n = 0; n < C::CPT; ++n) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (wid * C::CPT + n) * 1024);
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds"
-        :
-        : "s"(dst), "v"(base + voff[n]), "s"(rsrc)
-        : "memory", "m0");
+    dma16(lds0 + (wid * C::CPT + n) * 1024, base + voff[n], rsrc);
   }
-}
-
-// one V^T operand (32 d x 16 keys) by two transposing reads
-__device__ __forceinline__ u32x4 vt_operand(const uint8_t* p0, const uint8_t* p1) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
-  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 // Mask the S^T accumulators of the NKB 32-key blocks of a tile starting at key
@@ -710,15 +582,7 @@ void fwd8_kernel(FwdParams p) {
   const uint32_t vst1 = (uint32_t)crow * C::VROWB + (uint32_t)(((2 * cch + 1) ^ swz<D>(crow)) * 16);
   auto dma_k = [&](uint8_t* buf, uint32_t base) __attribute__((always_inline)) {
     if (has_chunk) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(lds_void*)buf + wid * 1024);
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "s_nop 0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds"
-          :
-          : "s"(dst), "v"(base + kdma), "s"(krs)
-          : "memory", "m0");
+      dma16((uint32_t)(uintptr_t)(lds_void*)buf + wid * 1024, base + kdma, krs);
     }
   };
   auto store_v = [&](uint8_t* buf, u32x4 c) __attribute__((always_inline)) {

@@ -1,0 +1,45 @@
+// Launch parameters shared by the C ABI (host) and the backward kernels.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "fwd_params.h"
+
+namespace vlgqa {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;     // workspace: rowsum(dout * o) per (row, head), f32, same layout as lse
+  void* dq;
+  void* dk;
+  void* dv;
+  // packed layout: sequence b spans rows cu[b] .. cu[b+1]; null for dense
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  // strides in elements: batch, row (token), head
+  int64_t q_bs, q_rs, q_hs;  // q, o, dout, dq
+  int64_t k_bs, k_rs, k_hs;  // k, v, dk, dv
+  int64_t l_bs, l_rs, l_hs;  // lse, delta
+  int32_t batch, heads, kv_heads, group;
+  int32_t seqlen_q, seqlen_k;  // dense extents (per-sequence lengths come from cu_* when given)
+  int32_t causal, window;
+  int32_t max_seqlen_q, max_seqlen_k;
+  // rowsum kernel: rows are (b, r, h) with b < d_batch, r < d_rows
+  int32_t d_batch, d_rows;
+  // filled by plan_bwd:
+  int32_t n_ktiles;   // ceil(max_seqlen_k / 128): key tiles of the dK/dV kernel
+  int32_t n_qtiles;   // ceil(max_seqlen_q / 128): query tiles of the dQ kernel
+  float score_mul;    // log2(e) / sqrt(D): scores into the log2 domain
+  float scale;        // 1 / sqrt(D)
+};
+
+bool plan_bwd(BwdParams& p, int head_dim);
+
+hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t stream);
+
+}  // namespace vlgqa

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <string>
 
+#include "bwd_params.h"
 #include "fwd_params.h"
 #include "vlgqa.h"
 
@@ -199,6 +200,134 @@ int flash_attention_fwd_fp8(const void* q, const void* k, const void* v, int64_t
     return fail(VLGQA_EINVAL, "q_scale", "scale products overflow or underflow f32");
   return dense_common(q, k, v, batch, num_heads, num_kv_heads, seqlen_q, seqlen_k, head_dim,
                       causal, 0, -1, vlgqa::E_E4M3, mul, omul, out, lse, hip_stream);
+}
+
+static int bwd_common(vlgqa::BwdParams& p, int dtype, int64_t head_dim, int64_t rows,
+                      void* hip_stream) {
+  int rc;
+  if (dtype != VLGQA_BF16 && dtype != VLGQA_F16) {
+    if (dtype == VLGQA_F32) return fail(VLGQA_EUNSUPPORTED, "dtype", "the backward is compiled for bf16 and f16 only");
+    return fail(VLGQA_EUNSUPPORTED, "dtype", "unknown dtype code");
+  }
+  if (rows > 0) {  // with no query rows only dk = dv = 0 are written
+    if ((rc = check_ptr(p.dout, "dout"))) return rc;
+    if ((rc = check_ptr(p.q, "q"))) return rc;
+    if ((rc = check_ptr(p.o, "out"))) return rc;
+    if ((rc = check_ptr(p.lse, "lse"))) return rc;
+    if ((rc = check_ptr(p.dq, "dq"))) return rc;
+    if ((rc = check_ptr(p.delta, "workspace"))) return rc;
+  }
+  p.score_mul = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  p.scale = (float)(1.0 / std::sqrt((double)head_dim));
+  if (!vlgqa::plan_bwd(p, (int)head_dim))
+    return fail(VLGQA_EINVAL, "max_seqlen_q", "problem too large for one launch");
+  const int elem = dtype == VLGQA_F16 ? vlgqa::E_F16 : vlgqa::E_BF16;
+  hipError_t e = vlgqa::launch_bwd(p, elem, (int)head_dim, reinterpret_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
+  return VLGQA_OK;
+}
+
+int varlen_attention_bwd(const void* dout, const void* q, const void* k, const void* v,
+                         const void* out, const float* lse, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k,
+                         int64_t batch_size, int64_t num_heads, int64_t num_kv_heads,
+                         int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t head_dim,
+                         int causal, int dtype, void* dq, void* dk, void* dv, float* workspace,
+                         void* hip_stream) {
+  g_last_error.clear();
+  int rc;
+  if (dtype != VLGQA_BF16 && dtype != VLGQA_F16 && dtype != VLGQA_F32)
+    return fail(VLGQA_EUNSUPPORTED, "dtype", "unknown dtype code");
+  if ((rc = check_head_dim(head_dim))) return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads))) return rc;
+  if (total_q < 0) return fail(VLGQA_EINVAL, "total_q", "must be non-negative");
+  if (total_k < 0) return fail(VLGQA_EINVAL, "total_k", "must be non-negative");
+  if (batch_size < 0) return fail(VLGQA_EINVAL, "batch_size", "must be non-negative");
+  if (max_seqlen_q < 0) return fail(VLGQA_EINVAL, "max_seqlen_q", "must be non-negative");
+  if (max_seqlen_k < 0) return fail(VLGQA_EINVAL, "max_seqlen_k", "must be non-negative");
+  if (causal != 0 && causal != 1) return fail(VLGQA_EINVAL, "causal", "must be 0 or 1");
+  if (total_q > INT32_MAX || total_k > INT32_MAX)
+    return fail(VLGQA_EINVAL, "total_q", "token counts must fit I32 cu_seqlens");
+  if (max_seqlen_q > INT32_MAX || max_seqlen_k > INT32_MAX)
+    return fail(VLGQA_EINVAL, "max_seqlen_q", "too large");
+  if (batch_size > INT32_MAX - 1) return fail(VLGQA_EINVAL, "batch_size", "too large");
+  if (batch_size == 0 || (total_q == 0 && total_k == 0)) return VLGQA_OK;
+  if (dtype == VLGQA_F32)
+    return fail(VLGQA_EUNSUPPORTED, "dtype", "the backward is compiled for bf16 and f16 only");
+  if ((rc = check_ptr(cu_seqlens_q, "cu_seqlens_q"))) return rc;
+  if ((rc = check_ptr(cu_seqlens_k, "cu_seqlens_k"))) return rc;
+  if (total_k > 0) {
+    if ((rc = check_ptr(k, "k"))) return rc;
+    if ((rc = check_ptr(v, "v"))) return rc;
+    if ((rc = check_ptr(dk, "dk"))) return rc;
+    if ((rc = check_ptr(dv, "dv"))) return rc;
+  }
+  vlgqa::BwdParams p{};
+  p.dout = dout; p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse; p.delta = workspace;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+  p.q_bs = 0; p.q_rs = num_heads * head_dim; p.q_hs = head_dim;
+  p.k_bs = 0; p.k_rs = num_kv_heads * head_dim; p.k_hs = head_dim;
+  p.l_bs = 0; p.l_rs = num_heads; p.l_hs = 1;
+  p.batch = (int32_t)batch_size;
+  p.heads = (int32_t)num_heads;
+  p.kv_heads = (int32_t)num_kv_heads;
+  p.group = (int32_t)(num_heads / num_kv_heads);
+  p.seqlen_q = 0; p.seqlen_k = 0;
+  p.causal = causal; p.window = 0;
+  p.max_seqlen_q = (int32_t)max_seqlen_q;
+  p.max_seqlen_k = (int32_t)max_seqlen_k;
+  p.d_batch = 1; p.d_rows = (int32_t)total_q;
+  return bwd_common(p, dtype, head_dim, total_q, hip_stream);
+}
+
+int flash_attention_bwd(const void* dout, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, int64_t batch, int64_t num_heads,
+                        int64_t num_kv_heads, int64_t seqlen_q, int64_t seqlen_k,
+                        int64_t head_dim, int causal, int64_t window_size, int dtype, void* dq,
+                        void* dk, void* dv, float* workspace, void* hip_stream) {
+  g_last_error.clear();
+  int rc;
+  if (dtype != VLGQA_BF16 && dtype != VLGQA_F16 && dtype != VLGQA_F32)
+    return fail(VLGQA_EUNSUPPORTED, "dtype", "unknown dtype code");
+  if ((rc = check_head_dim(head_dim))) return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads))) return rc;
+  if (batch < 0) return fail(VLGQA_EINVAL, "batch", "must be non-negative");
+  if (seqlen_q < 0) return fail(VLGQA_EINVAL, "seqlen_q", "must be non-negative");
+  if (seqlen_k < 0) return fail(VLGQA_EINVAL, "seqlen_k", "must be non-negative");
+  if (window_size < 0) return fail(VLGQA_EINVAL, "window_size", "must be non-negative");
+  if (causal != 0 && causal != 1) return fail(VLGQA_EINVAL, "causal", "must be 0 or 1");
+  if (seqlen_q > INT32_MAX || seqlen_k > INT32_MAX || batch > INT32_MAX)
+    return fail(VLGQA_EINVAL, "seqlen_q", "extents must fit 32 bits");
+  if (window_size > INT32_MAX) window_size = INT32_MAX;
+  if (batch == 0 || (seqlen_q == 0 && seqlen_k == 0)) return VLGQA_OK;
+  if (dtype == VLGQA_F32)
+    return fail(VLGQA_EUNSUPPORTED, "dtype", "the backward is compiled for bf16 and f16 only");
+  if (seqlen_k > 0) {
+    if ((rc = check_ptr(k, "k"))) return rc;
+    if ((rc = check_ptr(v, "v"))) return rc;
+    if ((rc = check_ptr(dk, "dk"))) return rc;
+    if ((rc = check_ptr(dv, "dv"))) return rc;
+  }
+  vlgqa::BwdParams p{};
+  p.dout = dout; p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse; p.delta = workspace;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.cu_q = nullptr; p.cu_k = nullptr;
+  p.q_bs = num_heads * seqlen_q * head_dim; p.q_rs = head_dim; p.q_hs = seqlen_q * head_dim;
+  p.k_bs = num_kv_heads * seqlen_k * head_dim; p.k_rs = head_dim; p.k_hs = seqlen_k * head_dim;
+  p.l_bs = num_heads * seqlen_q; p.l_rs = 1; p.l_hs = seqlen_q;
+  p.batch = (int32_t)batch;
+  p.heads = (int32_t)num_heads;
+  p.kv_heads = (int32_t)num_kv_heads;
+  p.group = (int32_t)(num_heads / num_kv_heads);
+  p.seqlen_q = (int32_t)seqlen_q;
+  p.seqlen_k = (int32_t)seqlen_k;
+  p.causal = causal;
+  p.window = (int32_t)window_size;
+  p.max_seqlen_q = (int32_t)seqlen_q;
+  p.max_seqlen_k = (int32_t)seqlen_k;
+  p.d_batch = (int32_t)batch; p.d_rows = (int32_t)seqlen_q;
+  return bwd_common(p, dtype, head_dim, batch * seqlen_q, hip_stream);
 }
 
 }  // extern "C"

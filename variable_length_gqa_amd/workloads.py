@@ -141,6 +141,13 @@ def make_dense(batch, num_heads, num_kv_heads, seqlen_q, head_dim, dtype=torch.b
                  None if kv_seq_len is None else n, name)
 
 
+def make_dout(like: torch.Tensor, seed: int) -> torch.Tensor:
+    """A seeded N(0,1) output gradient with the shape and dtype of ``like``
+    (the incoming gradient of a backward pass)."""
+    g = torch.Generator().manual_seed(seed)
+    return _normal(g, tuple(like.shape)).to(like.dtype)
+
+
 def quantize_e4m3(x: torch.Tensor):
     """Per-tensor E4M3 quantisation: (uint8 codes, scale) with scale = amax / 448."""
     amax = float(x.abs().max())
