@@ -1,7 +1,7 @@
 """Throughput of the fused varlen / GQA attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--cpu-heads N]
+                    [--pass forward|backward] [--no-cpu-baseline] [--cpu-heads N]
 
 One step = one call of the forward entry point over the whole workload (the
 complete hot path: a single fused kernel launch), inputs already resident in
@@ -13,6 +13,10 @@ Prints ONE JSON line.  FLOPs are algorithmic: 4*D per visible (query, key)
 pair per head, counted exactly from the sequence lengths and the mask.  Time
 comes from HIP events recorded on the stream the kernel runs on (torch's
 current stream), bracketed by device synchronisation.
+
+``--pass backward`` times one backward call instead (its three kernels; O
+and LSE from the GPU forward, computed once beforehand) and reports its own
+metric with 2.5x the forward's FLOPs (five products per visible pair).
 """
 
 from __future__ import annotations
@@ -28,21 +32,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "varlen causal GQA attn fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+METRIC_BWD = "varlen causal GQA attn bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["variable_length_gqa_amd/csrc/attn_fwd.hip",
-                  "variable_length_gqa_amd/csrc/fwd_params.h"]
+KERNEL_SOURCES = {
+    "forward": ["variable_length_gqa_amd/csrc/attn_fwd.hip",
+                "variable_length_gqa_amd/csrc/fwd_params.h",
+                "variable_length_gqa_amd/csrc/kernel_common.h"],
+    "backward": ["variable_length_gqa_amd/csrc/attn_bwd.hip",
+                 "variable_length_gqa_amd/csrc/bwd_params.h",
+                 "variable_length_gqa_amd/csrc/kernel_common.h"],
+}
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(which: str = "forward") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[which]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, which: str = "forward"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -51,8 +62,8 @@ def measured_traffic(workload: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    rec = t.get(workload)
-    if not rec or rec.get("kernel_source_digest") != kernel_source_digest():
+    rec = t.get(workload if which == "forward" else f"{workload}:{which}")
+    if not rec or rec.get("kernel_source_digest") != kernel_source_digest(which):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -115,6 +126,96 @@ def make_step(name, dev):
     return x, step, flops, io, cfg, dt
 
 
+def make_step_bwd(name, dev):
+    """One backward pass over the workload: dO seeded, O and LSE from the GPU
+    forward (computed once, outside the timed region), outputs preallocated."""
+    import torch
+
+    import variable_length_gqa_amd as vg
+    from variable_length_gqa_amd import flops as F
+    from variable_length_gqa_amd import workloads as W
+
+    x = W.workload(name)
+    if isinstance(x, W.Varlen):
+        xd = x.to(dev)
+        out, lse = vg.varlen_attention_fwd(xd.q, xd.k, xd.v, xd.cu_q, xd.cu_k, x.batch_size,
+                                           x.num_heads, x.num_kv_heads, x.max_seqlen_q,
+                                           x.max_seqlen_k, x.head_dim, x.causal)
+        dO = W.make_dout(x.q, 400).to(dev)
+        dq, dk, dv = torch.empty_like(xd.q), torch.empty_like(xd.k), torch.empty_like(xd.v)
+        ws = torch.empty(vg.attention.bwd_workspace_floats(xd.q.shape[0], xd.k.shape[0],
+                                                            x.num_heads, x.num_kv_heads,
+                                                            x.head_dim),
+                         dtype=torch.float32, device=dev)
+
+        def step():
+            vg.varlen_attention_bwd(dO, xd.q, xd.k, xd.v, out, lse, xd.cu_q, xd.cu_k,
+                                    x.batch_size, x.num_heads, x.num_kv_heads, x.max_seqlen_q,
+                                    x.max_seqlen_k, x.head_dim, x.causal, dq=dq, dk=dk, dv=dv,
+                                    workspace=ws)
+
+        flops = 2.5 * F.attention_flops(x.lengths_q, x.lengths_k, x.num_heads, x.head_dim,
+                                        x.causal)
+        cfg = {"workload": name, "pass": "backward", "layout": "packed varlen",
+               "lengths": x.lengths_q, "total_tokens": sum(x.lengths_q), "heads": x.num_heads,
+               "kv_heads": x.num_kv_heads, "head_dim": x.head_dim, "causal": x.causal}
+    else:
+        if x.scales or x.kv_seq_len not in (None, x.k.shape[2]):
+            raise SystemExit("the backward pass runs on bf16 / f16 workloads without a "
+                             "kv_seq_len shorter than the K/V buffer")
+        dd = x.to(dev)
+        B, H, Sq, D = x.q.shape
+        out, lse = vg.flash_attention_fwd(dd.q, dd.k, dd.v, H, x.num_kv_heads, D, x.causal,
+                                          x.window)
+        dO = W.make_dout(x.q, 400).to(dev)
+        dq, dk, dv = torch.empty_like(dd.q), torch.empty_like(dd.k), torch.empty_like(dd.v)
+        ws = torch.empty(vg.attention.bwd_workspace_floats(B * Sq, B * x.k.shape[2], H,
+                                                            x.num_kv_heads, D),
+                         dtype=torch.float32, device=dev)
+
+        def step():
+            vg.flash_attention_bwd(dO, dd.q, dd.k, dd.v, out, lse, H, x.num_kv_heads, D,
+                                   x.causal, x.window, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+        n = x.k.shape[2]
+        flops = 2.5 * F.attention_flops([Sq] * B, [n] * B, H, D, x.causal, x.window)
+        cfg = {"workload": name, "pass": "backward", "layout": "dense", "batch": B,
+               "seqlen_q": Sq, "seqlen_k": n, "heads": H, "kv_heads": x.num_kv_heads,
+               "head_dim": D, "causal": x.causal, "window": x.window}
+    dt = {torch.bfloat16: "bf16", torch.float16: "f16"}[x.q.dtype]
+    return x, step, int(flops), None, cfg, dt
+
+
+def cpu_baseline_bwd(name, x, n_heads, unit_scale):
+    """The f64 backward oracle on the first ``n_heads`` query heads (a bounded
+    sample of the same workload), all worker processes."""
+    import oracle
+    from oracle.attention import default_workers
+    from variable_length_gqa_amd import flops as F
+    from variable_length_gqa_amd import workloads as W
+
+    workers = default_workers()
+    heads = list(range(n_heads))
+    dO = W.make_dout(x.q, 400)
+    t0 = time.perf_counter()
+    if isinstance(x, W.Varlen):
+        oracle.varlen_attention_bwd(dO, x.q, x.k, x.v, x.cu_q, x.cu_k, x.num_heads,
+                                    x.num_kv_heads, x.causal, workers=workers, heads=heads)
+        fl = 2.5 * F.attention_flops(x.lengths_q, x.lengths_k, n_heads, x.head_dim, x.causal)
+    else:
+        B, H, Sq, D = x.q.shape
+        oracle.flash_attention_bwd(dO, x.q, x.k, x.v, H, x.num_kv_heads, x.causal, x.window,
+                                   workers=workers, heads=heads)
+        fl = 2.5 * F.attention_flops([Sq] * B, [x.k.shape[2]] * B, n_heads, D, x.causal,
+                                     x.window)
+    secs = time.perf_counter() - t0
+    return secs, {"value": fl / secs / unit_scale, "unit": "TFLOP/s", "cores": workers,
+                  "kind": "oracle",
+                  "sample": f"backward of query heads 0..{n_heads - 1} of {x.num_heads} of every "
+                            f"sequence ({fl:.3e} algorithmic FLOPs, {secs:.1f} s wall, f64 "
+                            f"NumPy, one process per core, masked scores computed too)"}
+
+
 def _fp8_o_scale():
     with open(os.path.join(ROOT, "tests", "golden", "fp8_o_scale.json")) as f:
         return json.load(f)["o_scale"]
@@ -164,6 +265,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="query heads in the CPU-baseline sample (0: sized to ~15 s)")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+                    help="the forward (the headline metric) or the backward pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -190,7 +293,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
                           "launches": max(1, args.steps)}), flush=True)
         return
-    x, step, flops, io, cfg, dt = make_step(args.workload, dev)
+    bwd = args.which == "backward"
+    x, step, flops, io, cfg, dt = (make_step_bwd if bwd else make_step)(args.workload, dev)
 
     for _ in range(args.warmup):
         step()
@@ -208,29 +312,32 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dt]
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload, args.which)
 
     res = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_BWD if bwd else METRIC, "value": round(tflops, 2), "unit": "TFLOP/s",
+        "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic (seeded N(0,1) inputs of the workload's shapes)",
         "config": cfg,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
-        "flops_per_step": flops, "io_bytes_per_step": io,
-        "io_gbs": round(io / (ms * 1e-3) / 1e9, 1), "wall_s_timed": round(wall, 3),
-        "kernel_source_digest": kernel_source_digest(),
+        "flops_per_step": flops, "wall_s_timed": round(wall, 3),
+        "kernel_source_digest": kernel_source_digest(args.which),
     }
+    if io is not None:
+        res["io_bytes_per_step"] = io
+        res["io_gbs"] = round(io / (ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
+        base = cpu_baseline_bwd if bwd else cpu_baseline
         n_heads = args.cpu_heads
         if n_heads <= 0:
             # size the sample to about 15 s: time one head group, then scale up
             G = x.num_heads // x.num_kv_heads
-            secs, _ = cpu_baseline(args.workload, x, min(G, x.num_heads), 1e12)
+            secs, _ = base(args.workload, x, min(G, x.num_heads), 1e12)
             n_heads = int(min(x.num_heads, max(G, G * round(15.0 / max(secs, 1e-3)))))
-        _, res["cpu_baseline"] = cpu_baseline(args.workload, x, min(n_heads, x.num_heads),
-                                              1e12)
+        _, res["cpu_baseline"] = base(args.workload, x, min(n_heads, x.num_heads), 1e12)
     print(json.dumps(res), flush=True)
 
 

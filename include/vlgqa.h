@@ -146,12 +146,15 @@ int flash_attention_fwd_fp8(const void* q, const void* k, const void* v,
  * are those of the forward.  dtype: VLGQA_BF16 or VLGQA_F16 (f32 and FP8 are
  * not compiled: EUNSUPPORTED); f32 accumulation, gradients stored in dtype.
  *
- * workspace: caller-allocated float32 scratch of 2 * (rows * num_heads)
- * floats, rows = total_q (packed) or batch * seqlen_q (dense), 16-byte
- * aligned.  On return it holds LSE * log2(e) (+inf for rows with no visible
- * key) and then delta, head-major ([num_heads][total_q], dense
- * [batch][num_heads][seqlen_q]).  Calls that share a workspace on one stream
- * are ordered by the stream; concurrent calls need separate workspaces.
+ * workspace: caller-allocated float32 scratch, 16-byte aligned, of
+ *     2 * rows * num_heads + 4 * keys * num_kv_heads * head_dim   floats,
+ * rows = total_q, keys = total_k (packed) or rows = batch * seqlen_q, keys =
+ * batch * seqlen_k (dense).  On return its first part holds LSE * log2(e)
+ * (+inf for rows with no visible key) and then delta, head-major
+ * ([num_heads][total_q], dense [batch][num_heads][seqlen_q]); the rest holds
+ * f32 partial sums of dk and dv.  It is required whenever the call has work.
+ * Calls that share a workspace on one stream are ordered by the stream;
+ * concurrent calls need separate workspaces.
  * dq, dk, dv are written in full (zero for rows / keys that take part in no
  * visible pair); padding outside the sequences is not written.
  */

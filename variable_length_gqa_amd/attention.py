@@ -195,14 +195,39 @@ def _check_bwd_common(dout, q, k, v, out, lse, dev):
     _need(lse.dtype == torch.float32, "lse must be float32")
 
 
+def bwd_workspace_floats(rows: int, keys: int, num_heads: int, num_kv_heads: int,
+                         head_dim: int) -> int:
+    """float32 elements of the backward workspace (see include/vlgqa.h)."""
+    return 2 * rows * num_heads + 4 * keys * num_kv_heads * head_dim
+
+
+def _bwd_outputs(q, k, v, dq, dk, dv, ws, ws_floats, dev):
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if ws is None:
+        ws = torch.empty((max(ws_floats, 4),), dtype=torch.float32, device=dev)
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_device_tensor(name, t, dev)
+        _need(t.shape == like.shape and t.dtype == like.dtype, f"{name} must match its input")
+    _check_device_tensor("workspace", ws, dev)
+    _need(ws.dtype == torch.float32 and ws.numel() >= ws_floats,
+          f"workspace must be float32 with at least {ws_floats} elements")
+    return dq, dk, dv, ws
+
+
 def varlen_attention_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          output: torch.Tensor, lse: torch.Tensor, cu_seqlens_q: torch.Tensor,
                          cu_seqlens_k: torch.Tensor, batch_size: int, num_heads: int,
                          num_kv_heads: int, max_seqlen_q: int, max_seqlen_k: int, head_dim: int,
-                         causal: bool, check_seqlens: bool | None = None):
+                         causal: bool, check_seqlens: bool | None = None,
+                         dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                         dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Packed variable-length attention backward -> (dq [total_q,H,D], dk, dv [total_k,Hkv,D]).
 
     ``output`` and ``lse`` are the forward's results for the same inputs.
+    dq / dk / dv / workspace (float32, ``bwd_workspace_floats(total_q, total_k,
+    ...)`` elements) may be passed preallocated.
     """
     dev = q.device
     _check_bwd_common(dout, q, k, v, output, lse, dev)
@@ -221,8 +246,9 @@ def varlen_attention_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v
     if check_seqlens if check_seqlens is not None else DEBUG_CHECKS:
         check_cu_seqlens(cu_seqlens_q, total_q, max_seqlen_q, "cu_seqlens_q")
         check_cu_seqlens(cu_seqlens_k, total_k, max_seqlen_k, "cu_seqlens_k")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty((2 * max(total_q, 1) * num_heads,), dtype=torch.float32, device=dev)
+    dq, dk, dv, ws = _bwd_outputs(q, k, v, dq, dk, dv, workspace,
+                                  bwd_workspace_floats(total_q, total_k, num_heads,
+                                                       num_kv_heads, head_dim), dev)
     lib = _lib.load()
     rc = lib.varlen_attention_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(output), _ptr(lse),
                                   _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), total_q, total_k,
@@ -236,10 +262,14 @@ def varlen_attention_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v
 
 def flash_attention_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         output: torch.Tensor, lse: torch.Tensor, num_heads: int,
-                        num_kv_heads: int, head_dim: int, causal: bool, window_size: int = 0):
+                        num_kv_heads: int, head_dim: int, causal: bool, window_size: int = 0,
+                        dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                        dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Dense attention backward -> (dq [B,H,S_q,D], dk, dv [B,Hkv,S_k,D]).
 
     All S_k keys of k/v are attended (the pages' backward takes no kv_seq_len).
+    dq / dk / dv / workspace (float32, ``bwd_workspace_floats(B * S_q, B * S_k,
+    ...)`` elements) may be passed preallocated.
     """
     dev = q.device
     _check_bwd_common(dout, q, k, v, output, lse, dev)
@@ -251,8 +281,9 @@ def flash_attention_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v:
     B, _, Sq, _ = q.shape
     Sk = k.shape[2]
     _need(lse.shape == (B, num_heads, Sq), "lse must be [B, num_heads, S_q]")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty((2 * max(B * Sq, 1) * num_heads,), dtype=torch.float32, device=dev)
+    dq, dk, dv, ws = _bwd_outputs(q, k, v, dq, dk, dv, workspace,
+                                  bwd_workspace_floats(B * Sq, B * Sk, num_heads, num_kv_heads,
+                                                       head_dim), dev)
     lib = _lib.load()
     rc = lib.flash_attention_bwd(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(output), _ptr(lse),
                                  B, num_heads, num_kv_heads, Sq, Sk, head_dim,

@@ -11,17 +11,18 @@
 //   dq_i  = scale sum_j dS_ij k_j,       dk_j = scale sum_i dS_ij q_i
 // with dk / dv of a kv head summed over its G query heads.
 //
-// Three launches:
+// Four launches:
 //   bwd_rowsum_kernel  delta_i = dO_i.O_i and LSE_i log2(e) per (row, head),
 //                      written head-major into the caller's workspace (so a
 //                      query tile's values are contiguous).
-//   bwd_dkdv_kernel    one workgroup per (sequence, kv head, 128-key tile),
-//                      4 waves x 32 keys; K and V of the wave's keys stay in
-//                      registers; the loop runs over the G query heads and the
-//                      32-row query tiles that see the keys, with Q, dO and the
+//   bwd_kv_kernel      dV, then dK (two launches of one body): one workgroup
+//                      per (sequence, kv head, 128-key tile), 4 waves x 32
+//                      keys; K (and V) of the wave's keys stay in registers;
+//                      the loop runs over the G query heads and the 32-row
+//                      query tiles that see the keys, with Q, dO and the
 //                      tile's LSE / delta brought to LDS by DMA (double
-//                      buffered).  dK and dV accumulate in registers: no atomics,
-//                      deterministic.
+//                      buffered).  dV / dK accumulate in registers: no
+//                      atomics, deterministic.
 //   bwd_dq_kernel      one workgroup per (sequence, 128-row query tile, query
 //                      head), the forward's structure: K/V tiles of 32 keys by
 //                      DMA into LDS, Q^T and dO^T in registers, dQ^T in
@@ -207,25 +208,39 @@ __device__ __forceinline__ void store_rows(void* base, int64_t row_off, int hl,
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV
+// dK and dV
 // ---------------------------------------------------------------------------
+//
+// Two launches of one kernel body, so that each fits at least two waves per
+// SIMD: MODE_DV computes S -> P -> dV^T += dO^T P (K^T of the lane's key in
+// registers, dV^T accumulators), MODE_DK computes S, dP -> dS -> dK^T +=
+// Q^T dS (K^T and V^T in registers, dK^T accumulators).  S is recomputed by
+// both (10 D + 2 D FLOPs per pair in the two launches instead of 8 D fused),
+// which costs less than running one fused kernel at one wave per SIMD.
+enum : int { MODE_DV = 0, MODE_DK = 1 };
 
-template <int ELEM, int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(BwdParams p) {
+template <int ELEM, int D, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(MODE == MODE_DV ? 3 : 2, MODE == MODE_DV ? 3 : 2)))
+void bwd_kv_kernel(BwdParams p) {
   using C = T16<D>;
   // stage buffer: Q tile, dO tile, then 32 lse2 + 32 delta floats
   constexpr int STAGE = 2 * C::TILE + 256;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
+  // work: (key tile ascending: more queries see the early keys, batch, kv
+  // head, split); one split covers group / n_split query heads
   const int BK = p.batch * p.kv_heads;
-  const int grp = blockIdx.x;
+  const int sp = blockIdx.x % p.n_split;
+  const int grp = blockIdx.x / p.n_split;
   const int kt = grp / BK;
   const int b = (grp % BK) / p.kv_heads;
   const int kvh = grp % p.kv_heads;
   const SeqBounds sb = seq_bounds(p, b);
   const int k0 = kt * kTileB;
   if (k0 >= sb.Lk) return;
+  const int gsplit = p.group / p.n_split;  // query heads of this workgroup
+  const int hbase = kvh * p.group + sp * gsplit;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
@@ -235,8 +250,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   const bool upper = p.causal || p.window > 0;
   const float mul = p.score_mul;
 
-  // K^T / V^T fragments of the lane's key: k[key][16 ks + 8 hl .. +8]
-  u32x4 kf[C::NS], vf[C::NS];
+  // K^T (and for dK V^T) fragments of the lane's key: k[key][16 ks + 8 hl .. +8]
+  u32x4 kf[C::NS], vf[MODE == MODE_DK ? C::NS : 1];
   {
     const int64_t koff = ((int64_t)b * p.k_bs + (int64_t)sb.k_start * p.k_rs +
                           (int64_t)kvh * p.k_hs) * 2;
@@ -247,15 +262,12 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < C::NS; ++ks) {
       kf[ks] = bload16(kr, roff + (16 * ks + 8 * hl) * 2);
-      vf[ks] = bload16(vr, roff + (16 * ks + 8 * hl) * 2);
+      if constexpr (MODE == MODE_DK) vf[ks] = bload16(vr, roff + (16 * ks + 8 * hl) * 2);
     }
   }
-  f32x16 dk[C::NOB], dv[C::NOB];
+  f32x16 acc[C::NOB];
 #pragma unroll
-  for (int i = 0; i < C::NOB; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
-  }
+  for (int i = 0; i < C::NOB; ++i) acc[i] = f32x16{};
 
   // query rows that see any key of the workgroup / of this wave
   const int k1 = min(k0 + kTileB, sb.Lk);
@@ -263,7 +275,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int qb = p.window > 0 ? min(sb.Lq, k1 - 1 - off + p.window) : sb.Lq;
   const int ta = qa / 32, tb = qb > qa ? (qb + 31) / 32 : ta;
   const int nt = tb - ta;
-  const int nst = nt * p.group;  // stages: (query head, query tile)
+  const int nst = nt * gsplit;  // stages: (query head, query tile)
   const int kw1 = min(kw + 32, sb.Lk);
   const bool wave_keys = kw < sb.Lk;
   const int wqa = upper ? max(0, kw - off) : 0;
@@ -279,7 +291,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   // DMA of stage s into buffer u: Q and dO tiles of (head, tile), lse2/delta
   auto issue = [&](int s, int u) __attribute__((always_inline)) {
     const int hh = s / nt, t = ta + s % nt;
-    const int h = kvh * p.group + hh;
+    const int h = hbase + hh;
     const int64_t qoff = ((int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs +
                           (int64_t)h * p.q_hs) * 2;
     const uint32_t bytes = sat_bytes((int64_t)sb.Lq * p.q_rs * 2);
@@ -317,14 +329,16 @@ void bwd_dkdv_kernel(BwdParams p) {
       for (int ks = 0; ks < C::NS; ++ks) {
         const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
         sc = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(qt + ro), kf[ks], sc);
-        dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(dot + ro), vf[ks], dp);
+        if constexpr (MODE == MODE_DK)
+          dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(dot + ro), vf[ks], dp);
       }
       // register r holds query row q0 + qq(r) + 4 hl, qq(r) = 8 (r / 4) + r % 4
       f32x4 l2[4], dl[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         l2[j] = *reinterpret_cast<const f32x4*>(wsv + 8 * j + 4 * hl);
-        dl[j] = *reinterpret_cast<const f32x4*>(wsv + 32 + 8 * j + 4 * hl);
+        if constexpr (MODE == MODE_DK)
+          dl[j] = *reinterpret_cast<const f32x4*>(wsv + 32 + 8 * j + 4 * hl);
       }
       const bool need_mask = key >= sb.Lk || q0 + 32 > sb.Lq ||
                              (upper && kw + 31 > q0 + off) ||
@@ -343,7 +357,8 @@ void bwd_dkdv_kernel(BwdParams p) {
           if (!kin || qq < lo || qq > hi) sc[r] = -INFINITY;
         }
       }
-      u32x4 pk[2], dsk[2];
+      // B operand of the accumulation: P (dV) or dS (dK), 16-bit
+      u32x4 bk[2];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
@@ -352,17 +367,20 @@ void bwd_dkdv_kernel(BwdParams p) {
           const int j = r >> 2, e = r & 3;
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], mul, -l2[j][e]));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r + 1], mul, -l2[j][e + 1]));
-          pk[t2][i] = pack2<ELEM>(p0, p1);
-          dsk[t2][i] = pack2<ELEM>(p0 * (dp[r] - dl[j][e]), p1 * (dp[r + 1] - dl[j][e + 1]));
+          if constexpr (MODE == MODE_DV)
+            bk[t2][i] = pack2<ELEM>(p0, p1);
+          else
+            bk[t2][i] = pack2<ELEM>(p0 * (dp[r] - dl[j][e]), p1 * (dp[r + 1] - dl[j][e + 1]));
         }
       }
+      // dV^T += dO^T P  or  dK^T += Q^T dS  (A by transposing reads)
+      const uint8_t* at = MODE == MODE_DV ? dot : qt;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
         for (int db = 0; db < C::NOB; ++db) {
           const uint32_t o0 = troff[db][0] + t2 * 16 * C::ROWB, o1 = troff[db][1] + t2 * 16 * C::ROWB;
-          dv[db] = mfma16<ELEM>(vt_operand(dot + o0, dot + o1), pk[t2], dv[db]);
-          dk[db] = mfma16<ELEM>(vt_operand(qt + o0, qt + o1), dsk[t2], dk[db]);
+          acc[db] = mfma16<ELEM>(vt_operand(at + o0, at + o1), bk[t2], acc[db]);
         }
       }
     }
@@ -371,11 +389,69 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (key < sb.Lk) {
-    const int64_t row = (int64_t)b * p.k_bs + (int64_t)(sb.k_start + key) * p.k_rs +
-                        (int64_t)kvh * p.k_hs;
-    store_rows<ELEM, D>(p.dk, row, hl, dk, p.scale);
-    store_rows<ELEM, D>(p.dv, row, hl, dv, 1.0f);
+    if (p.n_split == 1) {
+      const int64_t row = (int64_t)b * p.k_bs + (int64_t)(sb.k_start + key) * p.k_rs +
+                          (int64_t)kvh * p.k_hs;
+      if constexpr (MODE == MODE_DV)
+        store_rows<ELEM, D>(p.dv, row, hl, acc, 1.0f);
+      else
+        store_rows<ELEM, D>(p.dk, row, hl, acc, p.scale);
+    } else {
+      // f32 partial of this split: [mode][sp][kp_row][kvh][d]
+      const int64_t kp = (p.cu_k ? 0 : (int64_t)b * p.seqlen_k) + sb.k_start + key;
+      float* dst = p.part + ((((int64_t)(MODE == MODE_DV) * p.n_split + sp) * p.kp_rows + kp) *
+                             p.kv_heads + kvh) * D;
+#pragma unroll
+      for (int db = 0; db < C::NOB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v4 = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2],
+                            acc[db][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(dst + db * 32 + g * 8 + 4 * hl) = v4;
+        }
+    }
   }
+}
+
+// Sum the n_split partials of dK (times scale) and dV and store them in the
+// input dtype: one thread per (key row, kv head, 8 d).
+template <int ELEM, int D>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
+  const int64_t n = (int64_t)p.kp_rows * p.kv_heads * (D / 8);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int c = (int)(i % (D / 8));
+  const int64_t rk = i / (D / 8);           // kp_row * kv_heads + kvh
+  const int kvh = (int)(rk % p.kv_heads);
+  const int64_t kp = rk / p.kv_heads;
+  const int64_t plane = (int64_t)p.kp_rows * p.kv_heads * D;
+  float sk[8] = {}, sv[8] = {};
+  for (int sp = 0; sp < p.n_split; ++sp) {
+    const float* a = p.part + (int64_t)sp * plane + rk * D + c * 8;
+    const float* v = p.part + (int64_t)(p.n_split + sp) * plane + rk * D + c * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(a + 4 * h);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(v + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sk[4 * h + j] += x[j];
+        sv[4 * h + j] += y[j];
+      }
+    }
+  }
+  // packed: kp is the token row; dense: kp = b * seqlen_k + key
+  const int64_t b = p.cu_k ? 0 : kp / p.seqlen_k;
+  const int64_t key = p.cu_k ? kp : kp % p.seqlen_k;
+  const int64_t off = b * p.k_bs + key * p.k_rs + (int64_t)kvh * p.k_hs + c * 8;
+  u32x4 ok, ov;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ok[j] = pack2<ELEM>(sk[2 * j] * p.scale, sk[2 * j + 1] * p.scale);
+    ov[j] = pack2<ELEM>(sv[2 * j], sv[2 * j + 1]);
+  }
+  *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dk) + off) = ok;
+  *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dv) + off) = ov;
 }
 
 // ---------------------------------------------------------------------------
@@ -544,7 +620,12 @@ void bwd_dq_kernel(BwdParams p) {
 bool plan_bwd(BwdParams& p, int head_dim) {
   const int64_t nk = ((int64_t)p.max_seqlen_k + kTileB - 1) / kTileB;
   const int64_t nq = ((int64_t)p.max_seqlen_q + kTileB - 1) / kTileB;
-  if (nk * p.batch * p.kv_heads > INT32_MAX / 2) return false;
+  // Two workgroups per (kv head, key tile), each over half of the group's
+  // query heads, when the group has an even size: the first key tiles of a
+  // causal sequence carry the most work, and halving their loop brings the
+  // longest workgroup down to about the average load of a CU slot.
+  p.n_split = (p.group % 2 == 0 && p.part != nullptr) ? 2 : 1;
+  if (nk * p.batch * p.kv_heads * p.n_split > INT32_MAX / 2) return false;
   if (nq * p.batch * p.heads > INT32_MAX / 2) return false;
   p.n_ktiles = (int32_t)nk;
   p.n_qtiles = (int32_t)nq;
@@ -555,13 +636,19 @@ bool plan_bwd(BwdParams& p, int head_dim) {
 hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t stream) {
   const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
   const int ppb = 4 * (64 / (head_dim / 8));
-  const dim3 g0((unsigned)((pairs + ppb - 1) / ppb)), g1((unsigned)(p.n_ktiles * p.batch * p.kv_heads)),
-      g2((unsigned)(p.n_qtiles * p.batch * p.heads)), blk(kThreads);
+  const int64_t nred = (int64_t)p.kp_rows * p.kv_heads * (head_dim / 8);
+  const dim3 g0((unsigned)((pairs + ppb - 1) / ppb)),
+      g1((unsigned)(p.n_ktiles * p.batch * p.kv_heads * p.n_split)),
+      g2((unsigned)(p.n_qtiles * p.batch * p.heads)), g3((unsigned)((nred + 255) / 256)),
+      blk(kThreads);
 #define VLGQA_BWD(E, D)                                                        \
   do {                                                                         \
     if (pairs > 0) hipLaunchKernelGGL((bwd_rowsum_kernel<E, D>), g0, blk, 0, stream, p); \
-    if (g1.x > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), g1, blk, 0, stream, p);   \
+    if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DV>), g1, blk, 0, stream, p); \
+    if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DK>), g1, blk, 0, stream, p); \
     if (g2.x > 0) hipLaunchKernelGGL((bwd_dq_kernel<E, D>), g2, blk, 0, stream, p);     \
+    if (p.n_split > 1 && g3.x > 0)                                                       \
+      hipLaunchKernelGGL((bwd_reduce_kernel<E, D>), g3, blk, 0, stream, p);              \
   } while (0)
   if (head_dim == 128 && elem == E_BF16) VLGQA_BWD(E_BF16, 128);
   else if (head_dim == 128 && elem == E_F16) VLGQA_BWD(E_F16, 128);

@@ -31,7 +31,13 @@ struct BwdParams {
   int32_t max_seqlen_q, max_seqlen_k;
   // rowsum kernel: rows are (b, r, h) with b < d_batch, r < d_rows
   int32_t d_batch, d_rows;
+  // dK/dV partial sums (f32) when the query heads of a group are split over
+  // n_split workgroups: [2 (dk, dv)][n_split][kp_rows][kv_heads][D], summed by
+  // the reduction kernel; kp_rows = total_k (packed) or batch * seqlen_k
+  float* part;
+  int32_t kp_rows;
   // filled by plan_bwd:
+  int32_t n_split;    // workgroups per (kv head, key tile): 1 or 2
   int32_t n_ktiles;   // ceil(max_seqlen_k / 128): key tiles of the dK/dV kernel
   int32_t n_qtiles;   // ceil(max_seqlen_q / 128): query tiles of the dQ kernel
   float score_mul;    // log2(e) / sqrt(D): scores into the log2 domain

@@ -209,13 +209,13 @@ static int bwd_common(vlgqa::BwdParams& p, int dtype, int64_t head_dim, int64_t 
     if (dtype == VLGQA_F32) return fail(VLGQA_EUNSUPPORTED, "dtype", "the backward is compiled for bf16 and f16 only");
     return fail(VLGQA_EUNSUPPORTED, "dtype", "unknown dtype code");
   }
+  if ((rc = check_ptr(p.delta, "workspace"))) return rc;
   if (rows > 0) {  // with no query rows only dk = dv = 0 are written
     if ((rc = check_ptr(p.dout, "dout"))) return rc;
     if ((rc = check_ptr(p.q, "q"))) return rc;
     if ((rc = check_ptr(p.o, "out"))) return rc;
     if ((rc = check_ptr(p.lse, "lse"))) return rc;
     if ((rc = check_ptr(p.dq, "dq"))) return rc;
-    if ((rc = check_ptr(p.delta, "workspace"))) return rc;
   }
   p.score_mul = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   p.scale = (float)(1.0 / std::sqrt((double)head_dim));
@@ -278,6 +278,8 @@ int varlen_attention_bwd(const void* dout, const void* q, const void* k, const v
   p.max_seqlen_q = (int32_t)max_seqlen_q;
   p.max_seqlen_k = (int32_t)max_seqlen_k;
   p.d_batch = 1; p.d_rows = (int32_t)total_q;
+  p.kp_rows = (int32_t)total_k;
+  p.part = workspace ? workspace + 2 * total_q * num_heads : nullptr;
   return bwd_common(p, dtype, head_dim, total_q, hip_stream);
 }
 
@@ -327,6 +329,9 @@ int flash_attention_bwd(const void* dout, const void* q, const void* k, const vo
   p.max_seqlen_q = (int32_t)seqlen_q;
   p.max_seqlen_k = (int32_t)seqlen_k;
   p.d_batch = (int32_t)batch; p.d_rows = (int32_t)seqlen_q;
+  if (batch * seqlen_k > INT32_MAX) return fail(VLGQA_EINVAL, "seqlen_k", "batch * seqlen_k must fit 32 bits");
+  p.kp_rows = (int32_t)(batch * seqlen_k);
+  p.part = workspace ? workspace + 2 * batch * seqlen_q * num_heads : nullptr;
   return bwd_common(p, dtype, head_dim, batch * seqlen_q, hip_stream);
 }
 
