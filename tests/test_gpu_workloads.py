@@ -60,7 +60,7 @@ def test_varlen_bf16_gqa_full():
     o, l = _run_varlen(x)
     O, L = oracle.varlen_attention_fwd(x.q, x.k, x.v, x.cu_q, x.cu_k, 32, 8, True,
                                        workers=oracle_workers())
-    assert_close("O", to_f64(o), O, TOL[torch.bfloat16][0])
+    assert_close("O", to_f64(o), O, TOL[torch.bfloat16][0], torch.bfloat16)
     assert_close("LSE", l.double().numpy(), L, TOL[torch.bfloat16][1])
     _varlen_properties(x, o, l)
 
@@ -74,7 +74,7 @@ def test_varlen_bf16_long_sampled():
     O, L = oracle.varlen_rows(x.q, x.k, x.v, x.cu_q, x.cu_k, 64, 8, True, samples)
     got_o = np.stack([to_f64(o[int(x.cu_q[b]) + i, h]) for (b, h, i) in samples])
     got_l = np.array([float(l[int(x.cu_q[b]) + i, h]) for (b, h, i) in samples])
-    assert_close("O", got_o, O, TOL[torch.bfloat16][0])
+    assert_close("O", got_o, O, TOL[torch.bfloat16][0], torch.bfloat16)
     assert_close("LSE", got_l, L, TOL[torch.bfloat16][1])
 
 
@@ -96,7 +96,7 @@ def test_dense_bf16_window_sampled():
     O, L = oracle.dense_rows(d.q, d.k, d.v, 32, 8, True, samples, window=4096, kv_seq_len=8192)
     got_o = np.stack([to_f64(o[b, h, i]) for (b, h, i) in samples])
     got_l = np.array([float(l[b, h, i]) for (b, h, i) in samples])
-    assert_close("O", got_o, O, TOL[torch.bfloat16][0])
+    assert_close("O", got_o, O, TOL[torch.bfloat16][0], torch.bfloat16)
     assert_close("LSE", got_l, L, TOL[torch.bfloat16][1])
 
 
