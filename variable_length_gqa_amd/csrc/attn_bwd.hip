@@ -228,14 +228,20 @@ void bwd_kv_kernel(BwdParams p) {
   constexpr int STAGE = 2 * C::TILE + 256;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
-  // work: (key tile ascending: more queries see the early keys, batch, kv
-  // head, split); one split covers group / n_split query heads
-  const int BK = p.batch * p.kv_heads;
-  const int sp = blockIdx.x % p.n_split;
-  const int grp = blockIdx.x / p.n_split;
-  const int kt = grp / BK;
-  const int b = (grp % BK) / p.kv_heads;
-  const int kvh = grp % p.kv_heads;
+  // work: a "stream" is (batch, kv head, split) -- the query heads whose Q /
+  // dO it reads; one split covers group / n_split query heads.  Blocks go to
+  // the 8 XCDs round-robin; stream i always lands on XCD i % 8 (its key tiles
+  // share that XCD's L2), and each XCD runs its key tiles in ascending order
+  // (more queries see the early keys of a causal sequence: longest first).
+  const int nstream = p.batch * p.kv_heads * p.n_split;
+  const int per_xcd = (nstream + 7) / 8;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int kt = slot / per_xcd;
+  const int stream = (slot % per_xcd) * 8 + xcd;
+  if (stream >= nstream) return;
+  const int sp = stream % p.n_split;
+  const int kvh = (stream / p.n_split) % p.kv_heads;
+  const int b = stream / (p.n_split * p.kv_heads);
   const SeqBounds sb = seq_bounds(p, b);
   const int k0 = kt * kTileB;
   if (k0 >= sb.Lk) return;
@@ -275,7 +281,10 @@ void bwd_kv_kernel(BwdParams p) {
   const int qb = p.window > 0 ? min(sb.Lq, k1 - 1 - off + p.window) : sb.Lq;
   const int ta = qa / 32, tb = qb > qa ? (qb + 31) / 32 : ta;
   const int nt = tb - ta;
-  const int nst = nt * gsplit;  // stages: (query head, query tile)
+  // stages: (query head, query tile), the tiles from the last one down, so
+  // that the workgroups of one stream (which start at different tiles under a
+  // causal mask) read the same Q / dO tiles at about the same time
+  const int nst = nt * gsplit;
   const int kw1 = min(kw + 32, sb.Lk);
   const bool wave_keys = kw < sb.Lk;
   const int wqa = upper ? max(0, kw - off) : 0;
@@ -290,7 +299,7 @@ void bwd_kv_kernel(BwdParams p) {
 
   // DMA of stage s into buffer u: Q and dO tiles of (head, tile), lse2/delta
   auto issue = [&](int s, int u) __attribute__((always_inline)) {
-    const int hh = s / nt, t = ta + s % nt;
+    const int hh = s / nt, t = tb - 1 - s % nt;
     const int h = hbase + hh;
     const int64_t qoff = ((int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs +
                           (int64_t)h * p.q_hs) * 2;
@@ -318,7 +327,7 @@ void bwd_kv_kernel(BwdParams p) {
   for (int s = 0; s < nst; ++s) {
     const int u = s & 1;
     if (s + 1 < nst) issue(s + 1, u ^ 1);
-    const int t = ta + s % nt;
+    const int t = tb - 1 - s % nt;
     const int q0 = t * 32;
     if (wave_keys && q0 < wqb && q0 + 32 > wqa) {
       const uint8_t* qt = lds + u * STAGE;
@@ -467,15 +476,21 @@ void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lv0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lv1[C::TILE];
 
-  // work: (query tile descending, batch, head); heads of a kv group adjacent
-  const int grp = blockIdx.x;
-  const int h = grp % p.heads;
-  const int b = (grp / p.heads) % p.batch;
-  const int tq = p.n_qtiles - 1 - grp / (p.heads * p.batch);
+  // work, as in the forward: a group is (query tile, batch, kv head); its G
+  // query heads read the same K/V and sit on consecutive slots of one XCD
+  // (blocks go to the 8 XCDs round-robin); query tiles in descending order
+  // (under a causal mask later tiles see more keys: longest first)
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int gq = slot / p.group, hh = slot - gq * p.group;
+  const int grp = gq * 8 + xcd;
+  if (grp >= p.n_qtiles * p.batch * p.kv_heads) return;
+  const int kvh = grp % p.kv_heads;
+  const int b = (grp / p.kv_heads) % p.batch;
+  const int tq = p.n_qtiles - 1 - grp / (p.kv_heads * p.batch);
+  const int h = kvh * p.group + hh;
   const SeqBounds sb = seq_bounds(p, b);
   const int r0 = tq * kTileB;
   if (r0 >= sb.Lq) return;
-  const int kvh = h / p.group;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
@@ -625,8 +640,8 @@ bool plan_bwd(BwdParams& p, int head_dim) {
   // causal sequence carry the most work, and halving their loop brings the
   // longest workgroup down to about the average load of a CU slot.
   p.n_split = (p.group % 2 == 0 && p.part != nullptr) ? 2 : 1;
-  if (nk * p.batch * p.kv_heads * p.n_split > INT32_MAX / 2) return false;
-  if (nq * p.batch * p.heads > INT32_MAX / 2) return false;
+  if (nk * ((int64_t)p.batch * p.kv_heads * p.n_split + 8) > INT32_MAX / 2) return false;
+  if ((nq * p.batch * p.kv_heads + 8) * p.group > INT32_MAX / 2) return false;
   p.n_ktiles = (int32_t)nk;
   p.n_qtiles = (int32_t)nq;
   const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
@@ -637,10 +652,10 @@ hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t st
   const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
   const int ppb = 4 * (64 / (head_dim / 8));
   const int64_t nred = (int64_t)p.kp_rows * p.kv_heads * (head_dim / 8);
-  const dim3 g0((unsigned)((pairs + ppb - 1) / ppb)),
-      g1((unsigned)(p.n_ktiles * p.batch * p.kv_heads * p.n_split)),
-      g2((unsigned)(p.n_qtiles * p.batch * p.heads)), g3((unsigned)((nred + 255) / 256)),
-      blk(kThreads);
+  const int64_t streams8 = ((int64_t)p.batch * p.kv_heads * p.n_split + 7) / 8 * 8;
+  const int64_t groups8 = ((int64_t)p.n_qtiles * p.batch * p.kv_heads + 7) / 8 * 8;
+  const dim3 g0((unsigned)((pairs + ppb - 1) / ppb)), g1((unsigned)(p.n_ktiles * streams8)),
+      g2((unsigned)(groups8 * p.group)), g3((unsigned)((nred + 255) / 256)), blk(kThreads);
 #define VLGQA_BWD(E, D)                                                        \
   do {                                                                         \
     if (pairs > 0) hipLaunchKernelGGL((bwd_rowsum_kernel<E, D>), g0, blk, 0, stream, p); \
