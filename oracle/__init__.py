@@ -27,6 +27,7 @@ Modules:
   e4m3       -- OCP FP8 E4M3 ("fn") decode and round-to-nearest-even encode.
   backward   -- the gradient of the forward definition (dq, dk, dv), summed
                 over the query heads of a GQA group for dk/dv.
+  pack       -- padded [B, S, ...] <-> packed [total, ...] by cu_seqlens.
 
 Parity pins for every function live in ``tests/test_oracle_pins.py``; none of
 them compares the oracle with itself.
@@ -44,4 +45,4 @@ from .attention import (  # noqa: F401
     fp8_rows,
 )
 from .backward import attend_rows_bwd, varlen_attention_bwd, flash_attention_bwd  # noqa: F401
-from . import brute, online, e4m3  # noqa: F401
+from . import brute, online, e4m3, pack  # noqa: F401
