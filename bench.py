@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "varlen causal GQA attn fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 METRIC_BWD = "varlen causal GQA attn bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+METRIC_PACK = "padded <-> packed varlen copy GB/s on 1 MI355X; % of HBM peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {
@@ -42,6 +43,7 @@ KERNEL_SOURCES = {
     "backward": ["variable_length_gqa_amd/csrc/attn_bwd.hip",
                  "variable_length_gqa_amd/csrc/bwd_params.h",
                  "variable_length_gqa_amd/csrc/kernel_common.h"],
+    "pack": ["variable_length_gqa_amd/csrc/pack.hip"],
 }
 
 
@@ -186,6 +188,73 @@ def make_step_bwd(name, dev):
     return x, step, int(flops), None, cfg, dt
 
 
+def make_step_pack(name, dev, which):
+    """Pack (padded [B, S, H, D] -> packed) or unpack of the workload's q: the
+    step before / after the varlen forward.  Bytes are the algorithmic ones:
+    each valid row read and written once (unpack also writes the padding)."""
+    import torch
+
+    from variable_length_gqa_amd import packing
+    from variable_length_gqa_amd import workloads as W
+
+    x = W.workload(name)
+    if not isinstance(x, W.Varlen):
+        raise SystemExit("pack / unpack run on the packed workloads")
+    B, S = x.batch_size, x.max_seqlen_q
+    padded = torch.zeros((B, S) + tuple(x.q.shape[1:]), dtype=x.q.dtype)
+    cu = x.cu_q.tolist()
+    for b in range(B):
+        padded[b, :cu[b + 1] - cu[b]] = x.q[cu[b]:cu[b + 1]]
+    padded = padded.to(dev)
+    cud = x.cu_q.to(dev)
+    total = cu[-1]
+    packed = torch.empty((total,) + tuple(x.q.shape[1:]), dtype=x.q.dtype, device=dev)
+    row = x.q[0].numel() * x.q.element_size()
+    if which == "pack":
+        def step():
+            packing.pack(padded, cud, total=total, out=packed)
+        nbytes = 2 * total * row
+    else:
+        packing.pack(padded, cud, total=total, out=packed)
+        out = torch.empty_like(padded)
+
+        def step():
+            packing.unpack(packed, cud, S, out=out)
+        nbytes = total * row + B * S * row
+    cfg = {"workload": name, "pass": which, "batch": B, "max_seqlen": S,
+           "total_tokens": total, "row_bytes": row}
+    dt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[x.q.dtype]
+    return x, step, nbytes, padded, cfg, dt
+
+
+def cpu_baseline_pack(x, which, padded_dev):
+    """The NumPy packing oracle on the whole workload (one process)."""
+    import numpy as np
+
+    from oracle import pack as P
+
+    padded = padded_dev.cpu().view(torch_int16()).numpy()
+    lengths = [int(n) for n in np.diff(x.cu_q.numpy())]
+    t0 = time.perf_counter()
+    packed = P.pack(padded, lengths)
+    if which == "unpack":
+        t0 = time.perf_counter()
+        P.unpack(packed, x.cu_q.numpy(), padded.shape[1])
+    secs = time.perf_counter() - t0
+    row = padded[0, 0].nbytes
+    nbytes = 2 * packed.shape[0] * row if which == "pack" else \
+        packed.shape[0] * row + padded.shape[0] * padded.shape[1] * row
+    return {"value": nbytes / secs / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload's q ({nbytes / 1e6:.0f} MB moved, {secs:.2f} s, "
+                      f"NumPy, one thread)"}
+
+
+def torch_int16():
+    import torch
+
+    return torch.int16
+
+
 def cpu_baseline_bwd(name, x, n_heads, unit_scale):
     """The f64 backward oracle on the first ``n_heads`` query heads (a bounded
     sample of the same workload), all worker processes."""
@@ -265,8 +334,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="query heads in the CPU-baseline sample (0: sized to ~15 s)")
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
-                    help="the forward (the headline metric) or the backward pass")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "pack", "unpack"),
+                    default="forward",
+                    help="the forward (the headline metric), the backward pass, or the "
+                         "padded <-> packed copies")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -294,6 +365,8 @@ def main():
                           "launches": max(1, args.steps)}), flush=True)
         return
     bwd = args.which == "backward"
+    if args.which in ("pack", "unpack"):
+        return bench_pack(args, dev)
     x, step, flops, io, cfg, dt = (make_step_bwd if bwd else make_step)(args.workload, dev)
 
     for _ in range(args.warmup):
@@ -338,6 +411,50 @@ def main():
             secs, _ = base(args.workload, x, min(G, x.num_heads), 1e12)
             n_heads = int(min(x.num_heads, max(G, G * round(15.0 / max(secs, 1e-3)))))
         _, res["cpu_baseline"] = base(args.workload, x, min(n_heads, x.num_heads), 1e12)
+    print(json.dumps(res), flush=True)
+
+
+def bench_pack(args, dev):
+    import torch
+
+    x, step, nbytes, padded, cfg, dt = make_step_pack(args.workload, dev, args.which)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # reference: a plain device-to-device copy moving the same bytes (half read, half written)
+    src = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = nbytes / (ev0.elapsed_time(ev1) / args.steps * 1e-3) / 1e9
+    del src, dst
+    res = {
+        "metric": METRIC_PACK, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shapes)", "config": cfg,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "bytes_per_step": nbytes, "copy_reference_gbs": round(copy_gbs, 1),
+        "kernel_source_digest": kernel_source_digest("pack"),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_pack(x, args.which, padded)
     print(json.dumps(res), flush=True)
 
 

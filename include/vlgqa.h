@@ -202,6 +202,50 @@ int flash_attention_bwd(const void* dout, const void* q, const void* k, const vo
                         int causal, int64_t window_size, int dtype,
                         void* dq, void* dk, void* dv, float* workspace, void* hip_stream);
 
+/*
+ * Packing of padded batches into the varlen layout.
+ * boostr 0.2.0, src/ops/traits/attention/varlen_attention.rs: sequences of
+ * different lengths are packed into one buffer instead of being padded, and
+ * "Cumulative sequence lengths": cu_seqlens[0] = 0, cu_seqlens[i] = sum of
+ * the lengths of sequences 0..i-1 (the CSR offsets that boostr's MoE dispatch
+ * builds as a cumulative sum with a leading zero).  Pure data movement; rows
+ * are opaque bytes, so any dtype and head layout works.
+ */
+
+/*
+ * cu_seqlens [batch_size + 1] int32 (device) from lengths [batch_size] int32
+ * (device): the exclusive prefix sum followed by the total.  The lengths are
+ * trusted device memory: they must be non-negative with a sum that fits
+ * int32.  Errors: EINVAL for a negative batch_size or a null / misaligned
+ * pointer (lengths may be null when batch_size is 0).
+ */
+int vlgqa_cu_seqlens(const int32_t* lengths, int64_t batch_size, int32_t* cu_seqlens,
+                     void* hip_stream);
+
+/*
+ * Pack: packed row cu_seqlens[b] + s  <-  padded row (b, s), for every s <
+ * length_b = cu_seqlens[b+1] - cu_seqlens[b].
+ *   padded   [batch_size, max_seqlen, row_bytes]  (a row = one token's heads x
+ *            head_dim elements; row_bytes a multiple of 16)
+ *   packed   [total, row_bytes], total = cu_seqlens[batch_size]
+ *   cu_seqlens  device int32, trusted: non-decreasing, cu[0] = 0, each length
+ *            <= max_seqlen.
+ * Padding rows are not read; rows of packed past total are not written.
+ * Errors: EINVAL for negative extents, total > INT32_MAX, row_bytes not a
+ * positive multiple of 16, null or misaligned pointers with work to do.
+ */
+int vlgqa_pack(const void* padded, const int32_t* cu_seqlens, int64_t batch_size,
+               int64_t max_seqlen, int64_t row_bytes, int64_t total, void* packed,
+               void* hip_stream);
+
+/*
+ * Unpack: padded row (b, s) <- packed row cu_seqlens[b] + s for s < length_b,
+ * zero bytes for length_b <= s < max_seqlen.  Every padded row is written.
+ * Same layouts and errors as vlgqa_pack.
+ */
+int vlgqa_unpack(const void* packed, const int32_t* cu_seqlens, int64_t batch_size,
+                 int64_t max_seqlen, int64_t row_bytes, void* padded, void* hip_stream);
+
 /* "argument: reason" for the last non-OK return on this thread ("" if none). */
 const char* vlgqa_last_error(void);
 

@@ -232,3 +232,39 @@ def test_bwd_empty_problems_return_ok_without_pointers(lib):
     assert dense_bwd(lib, b=0, **none) == _lib.VLGQA_OK
     assert dense_bwd(lib, sq=0, sk=0, **none) == _lib.VLGQA_OK
     assert err(lib) == ""
+
+
+# --------------------------------------------------------------------------
+# packing entry points
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kw,code,arg", [
+    (dict(b=-1), EINVAL, "batch_size"),
+    (dict(s=-1), EINVAL, "max_seqlen"),
+    (dict(rb=24), EINVAL, "row_bytes"),
+    (dict(rb=0), EINVAL, "row_bytes"),
+    (dict(t=-1), EINVAL, "total"),
+    (dict(t=1 << 31), EINVAL, "total"),
+    (dict(cu=0), EINVAL, "cu_seqlens"),
+    (dict(pad=MIS), EINVAL, "padded"),
+    (dict(pk=0), EINVAL, "packed"),
+])
+def test_pack_rejects(lib, kw, code, arg):
+    a = dict(pad=A, cu=A, b=3, s=512, rb=256, t=940, pk=A)
+    a.update(kw)
+    assert lib.vlgqa_pack(a["pad"], a["cu"], a["b"], a["s"], a["rb"], a["t"], a["pk"], None) == code
+    assert err(lib).startswith(arg + ":"), err(lib)
+
+
+def test_unpack_and_cu_seqlens_reject(lib):
+    assert lib.vlgqa_unpack(A, A, 3, 512, 100, A, None) == EINVAL
+    assert err(lib).startswith("row_bytes:")
+    assert lib.vlgqa_unpack(A, A, 3, 512, 256, MIS, None) == EINVAL
+    assert err(lib).startswith("padded:")
+    assert lib.vlgqa_cu_seqlens(A, -1, A, None) == EINVAL
+    assert lib.vlgqa_cu_seqlens(0, 4, A, None) == EINVAL
+    assert err(lib).startswith("lengths:")
+    assert lib.vlgqa_cu_seqlens(A, 4, 0, None) == EINVAL
+    # nothing to move: OK without pointers
+    assert lib.vlgqa_pack(0, 0, 0, 512, 256, 0, 0, None) == _lib.VLGQA_OK
+    assert lib.vlgqa_unpack(0, A, 3, 0, 256, 0, None) == _lib.VLGQA_OK

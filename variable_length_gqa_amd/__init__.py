@@ -8,6 +8,8 @@ Entry points (HIP kernels for gfx950 behind a C ABI, see include/vlgqa.h):
   varlen_attention_bwd     gradients of the packed forward
   flash_attention_bwd      gradients of the dense forward
       -> (dq, dk, dv)
+  packing.cu_seqlens / packing.pack / packing.unpack
+                           lengths -> cu_seqlens, padded <-> packed on the device
 """
 
 from .attention import (  # noqa: F401
@@ -17,6 +19,7 @@ from .attention import (  # noqa: F401
     varlen_attention_bwd,
     varlen_attention_fwd,
 )
+from . import packing  # noqa: F401
 from ._lib import VlgqaError  # noqa: F401
 
 __version__ = "0.1.0"

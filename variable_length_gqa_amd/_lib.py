@@ -24,6 +24,9 @@ SIGNATURES = {
                                      _F, _F, _P, _P, _P]),
     "varlen_attention_bwd": (_I, [_P] * 8 + [_I64] * 8 + [_I, _I] + [_P] * 5),
     "flash_attention_bwd": (_I, [_P] * 6 + [_I64] * 6 + [_I, _I64, _I] + [_P] * 5),
+    "vlgqa_cu_seqlens": (_I, [_P, _I64, _P, _P]),
+    "vlgqa_pack": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P]),
+    "vlgqa_unpack": (_I, [_P, _P, _I64, _I64, _I64, _P, _P]),
     "vlgqa_last_error": (ctypes.c_char_p, []),
     "vlgqa_version": (ctypes.c_char_p, []),
 }

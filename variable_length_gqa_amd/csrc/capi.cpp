@@ -10,6 +10,7 @@
 
 #include "bwd_params.h"
 #include "fwd_params.h"
+#include "pack_api.h"
 #include "vlgqa.h"
 
 namespace {
@@ -333,6 +334,66 @@ int flash_attention_bwd(const void* dout, const void* q, const void* k, const vo
   p.kp_rows = (int32_t)(batch * seqlen_k);
   p.part = workspace ? workspace + 2 * batch * seqlen_q * num_heads : nullptr;
   return bwd_common(p, dtype, head_dim, batch * seqlen_q, hip_stream);
+}
+
+static int check_pack_common(const int32_t* cu_seqlens, int64_t batch_size, int64_t max_seqlen,
+                             int64_t row_bytes) {
+  int rc;
+  if (batch_size < 0) return fail(VLGQA_EINVAL, "batch_size", "must be non-negative");
+  if (batch_size > INT32_MAX - 1) return fail(VLGQA_EINVAL, "batch_size", "too large");
+  if (max_seqlen < 0) return fail(VLGQA_EINVAL, "max_seqlen", "must be non-negative");
+  if (max_seqlen > INT32_MAX) return fail(VLGQA_EINVAL, "max_seqlen", "too large");
+  if (row_bytes <= 0 || row_bytes % 16 != 0)
+    return fail(VLGQA_EINVAL, "row_bytes", "must be a positive multiple of 16");
+  if (row_bytes > ((int64_t)1 << 40) / (max_seqlen > 0 ? max_seqlen : 1) / (batch_size > 0 ? batch_size : 1))
+    return fail(VLGQA_EINVAL, "row_bytes", "padded buffer too large");
+  if (batch_size > 0 && (rc = check_ptr(cu_seqlens, "cu_seqlens"))) return rc;
+  return VLGQA_OK;
+}
+
+int vlgqa_cu_seqlens(const int32_t* lengths, int64_t batch_size, int32_t* cu_seqlens,
+                     void* hip_stream) {
+  g_last_error.clear();
+  int rc;
+  if (batch_size < 0) return fail(VLGQA_EINVAL, "batch_size", "must be non-negative");
+  if (batch_size > INT32_MAX - 1) return fail(VLGQA_EINVAL, "batch_size", "too large");
+  if ((rc = check_ptr(cu_seqlens, "cu_seqlens"))) return rc;
+  if (batch_size > 0 && (rc = check_ptr(lengths, "lengths"))) return rc;
+  hipError_t e = vlgqa::launch_cu_seqlens(lengths, batch_size, cu_seqlens,
+                                          reinterpret_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
+  return VLGQA_OK;
+}
+
+int vlgqa_pack(const void* padded, const int32_t* cu_seqlens, int64_t batch_size,
+               int64_t max_seqlen, int64_t row_bytes, int64_t total, void* packed,
+               void* hip_stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pack_common(cu_seqlens, batch_size, max_seqlen, row_bytes))) return rc;
+  if (total < 0) return fail(VLGQA_EINVAL, "total", "must be non-negative");
+  if (total > INT32_MAX) return fail(VLGQA_EINVAL, "total", "must fit I32 cu_seqlens");
+  if (batch_size == 0 || total == 0) return VLGQA_OK;
+  if ((rc = check_ptr(padded, "padded"))) return rc;
+  if ((rc = check_ptr(packed, "packed"))) return rc;
+  hipError_t e = vlgqa::launch_pack(padded, cu_seqlens, batch_size, max_seqlen, row_bytes, total,
+                                    packed, reinterpret_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
+  return VLGQA_OK;
+}
+
+int vlgqa_unpack(const void* packed, const int32_t* cu_seqlens, int64_t batch_size,
+                 int64_t max_seqlen, int64_t row_bytes, void* padded, void* hip_stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pack_common(cu_seqlens, batch_size, max_seqlen, row_bytes))) return rc;
+  if (batch_size == 0 || max_seqlen == 0) return VLGQA_OK;
+  if ((rc = check_ptr(packed, "packed"))) return rc;
+  if ((rc = check_ptr(padded, "padded"))) return rc;
+  hipError_t e = vlgqa::launch_unpack(packed, cu_seqlens, batch_size, max_seqlen, row_bytes,
+                                      padded, reinterpret_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
+  return VLGQA_OK;
 }
 
 }  // extern "C"
