@@ -1,7 +1,8 @@
 """Throughput of the fused varlen / GQA attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--pass forward|backward] [--no-cpu-baseline] [--cpu-heads N]
+                    [--pass forward|backward|decode|pack|unpack] [--no-cpu-baseline]
+                    [--cpu-heads N]
 
 One step = one call of the forward entry point over the whole workload (the
 complete hot path: a single fused kernel launch), inputs already resident in
@@ -13,6 +14,10 @@ Prints ONE JSON line.  FLOPs are algorithmic: 4*D per visible (query, key)
 pair per head, counted exactly from the sequence lengths and the mask.  Time
 comes from HIP events recorded on the stream the kernel runs on (torch's
 current stream), bracketed by device synchronisation.
+
+``--pass decode`` times the split-KV decode entry point on the KV-cache
+workload (one query per sequence against 8192 cached keys) in GB/s against
+HBM; ``--pass pack|unpack`` the padded <-> packed copies.
 
 ``--pass backward`` times one backward call instead (its three kernels; O
 and LSE from the GPU forward, computed once beforehand) and reports its own
@@ -34,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "varlen causal GQA attn fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 METRIC_BWD = "varlen causal GQA attn bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 METRIC_PACK = "padded <-> packed varlen copy GB/s on 1 MI355X; % of HBM peak"
+METRIC_DECODE = "KV-cache decode attn fwd GB/s on 1 MI355X; % of HBM peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {
@@ -44,6 +50,9 @@ KERNEL_SOURCES = {
                  "variable_length_gqa_amd/csrc/bwd_params.h",
                  "variable_length_gqa_amd/csrc/kernel_common.h"],
     "pack": ["variable_length_gqa_amd/csrc/pack.hip"],
+    "decode": ["variable_length_gqa_amd/csrc/decode.hip",
+               "variable_length_gqa_amd/csrc/decode_params.h",
+               "variable_length_gqa_amd/csrc/kernel_common.h"],
 }
 
 
@@ -334,10 +343,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="query heads in the CPU-baseline sample (0: sized to ~15 s)")
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "pack", "unpack"),
+    ap.add_argument("--pass", dest="which",
+                    choices=("forward", "backward", "pack", "unpack", "decode"),
                     default="forward",
-                    help="the forward (the headline metric), the backward pass, or the "
-                         "padded <-> packed copies")
+                    help="the forward (the headline metric), the backward pass, the "
+                         "padded <-> packed copies, or the split-KV decode path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -367,6 +377,8 @@ def main():
     bwd = args.which == "backward"
     if args.which in ("pack", "unpack"):
         return bench_pack(args, dev)
+    if args.which == "decode":
+        return bench_decode(args, dev)
     x, step, flops, io, cfg, dt = (make_step_bwd if bwd else make_step)(args.workload, dev)
 
     for _ in range(args.warmup):
@@ -455,6 +467,97 @@ def bench_pack(args, dev):
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_pack(x, args.which, padded)
+    print(json.dumps(res), flush=True)
+
+
+def decode_bytes(x):
+    """Algorithmic HBM bytes of one decode call: every visible K and V row of
+    each (batch, kv head) read once, q read and out written once, lse written."""
+    from variable_length_gqa_amd import flops as F
+
+    B, H, Sq, D = x.q.shape
+    n = x.kv_seq_len if x.kv_seq_len is not None else x.k.shape[2]
+    eb = x.q.element_size()
+    keys = F.visible_key_span(Sq, n, x.causal, x.window)
+    return 2 * B * x.num_kv_heads * keys * D * eb + 2 * B * H * Sq * D * eb + B * H * Sq * 4
+
+
+def cpu_baseline_decode(x):
+    """The f64 dense-forward oracle on the whole decode workload, all worker
+    processes, reported in the GPU metric's unit (the workload's algorithmic
+    bytes over the oracle's wall time)."""
+    import oracle
+    from oracle.attention import default_workers
+
+    workers = default_workers()
+    t0 = time.perf_counter()
+    oracle.flash_attention_fwd(x.q, x.k, x.v, x.num_heads, x.num_kv_heads, x.causal, x.window,
+                               x.kv_seq_len, workers=workers)
+    secs = time.perf_counter() - t0
+    nb = decode_bytes(x)
+    return {"value": nb / secs / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"the whole workload ({nb / 1e6:.0f} MB of algorithmic traffic, "
+                      f"{secs:.1f} s wall, f64 NumPy, one process per core)"}
+
+
+def bench_decode(args, dev):
+    import torch
+
+    import variable_length_gqa_amd as vg
+    from variable_length_gqa_amd import flops as F
+    from variable_length_gqa_amd import workloads as W
+
+    name = args.workload if args.workload != "varlen_bf16_long" else "dense_bf16_decode"
+    x = W.workload(name)
+    if not isinstance(x, W.Dense) or x.scales:
+        raise SystemExit("--pass decode runs on a dense 16-bit workload")
+    dd = x.to(dev)
+    B, H, Sq, D = x.q.shape
+    cap = x.k.shape[2]
+    n = x.kv_seq_len if x.kv_seq_len is not None else cap
+    out = torch.empty_like(dd.q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    ws = torch.empty(vg.decode_workspace_floats(B, x.num_kv_heads, D, cap), dtype=torch.float32,
+                     device=dev)
+
+    def step():
+        vg.flash_attention_decode(dd.q, dd.k, dd.v, H, x.num_kv_heads, D, x.causal, x.window,
+                                  x.kv_seq_len, out=out, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    nb = decode_bytes(x)
+    gbs = nb / (ms * 1e-3) / 1e9
+    flops = F.attention_flops([Sq] * B, [n] * B, H, D, x.causal, x.window)
+    dt = {torch.bfloat16: "bf16", torch.float16: "f16"}[x.q.dtype]
+    cfg = {"workload": name, "layout": "dense", "batch": B, "seqlen_q": Sq, "kv_seq_len": n,
+           "kv_capacity": cap, "heads": H, "kv_heads": x.num_kv_heads, "head_dim": D,
+           "causal": x.causal, "window": x.window}
+    res = {
+        "metric": METRIC_DECODE, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shapes)", "config": cfg,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(name, "decode")},
+        "bytes_per_step": nb, "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "wall_s_timed": round(wall, 3), "kernel_source_digest": kernel_source_digest("decode"),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(x)
     print(json.dumps(res), flush=True)
 
 

@@ -108,6 +108,42 @@ int flash_attention_fwd(const void* q, const void* k, const void* v,
                         int dtype, void* out, float* lse, void* hip_stream);
 
 /*
+ * Decode-shaped dense forward over a KV cache (split-KV).  Same operation,
+ * layouts, masks and results as flash_attention_fwd (boostr, src/ops/traits/
+ * attention/flash.rs, FlashAttentionOps::flash_attention_fwd, "kv_seq_len":
+ * a full-capacity cache buffer is attended up to n positions without
+ * narrowing), for a few new queries per sequence: it requires
+ * seqlen_q * (num_heads / num_kv_heads) <= 32.  The keys of each (batch, kv
+ * head) are split into slices that run in parallel; each slice writes an
+ * unnormalised partial output with its softmax maximum and denominator to the
+ * workspace, and a second kernel merges the slices by their log-sum-exp.
+ *
+ *   workspace  caller-allocated float32 scratch, 16-byte aligned, of at least
+ *              vlgqa_decode_workspace_floats(batch, num_kv_heads, head_dim, n)
+ *              floats, n = the attended length.  That size never decreases
+ *              as n grows, so a workspace sized for kv_capacity serves every
+ *              n.  Contents on return are unspecified; calls sharing one
+ *              workspace are ordered by their stream, concurrent calls need
+ *              separate workspaces.
+ *   workspace_floats  its size in floats.
+ *   dtype      VLGQA_BF16 or VLGQA_F16 (f32: EUNSUPPORTED).
+ *
+ * Errors: as flash_attention_fwd, plus EINVAL for seqlen_q * group > 32 or a
+ * workspace that is too small or null / misaligned.
+ */
+int flash_attention_decode(const void* q, const void* k, const void* v,
+                           int64_t batch, int64_t num_heads, int64_t num_kv_heads,
+                           int64_t seqlen_q, int64_t kv_capacity, int64_t head_dim,
+                           int causal, int64_t window_size, int64_t kv_seq_len,
+                           int dtype, void* out, float* lse, float* workspace,
+                           int64_t workspace_floats, void* hip_stream);
+
+/* Workspace floats flash_attention_decode needs for an attended length kv_len
+ * (-1 for a negative argument).  Host-only arithmetic. */
+int64_t vlgqa_decode_workspace_floats(int64_t batch, int64_t num_kv_heads, int64_t head_dim,
+                                      int64_t kv_len);
+
+/*
  * FP8 (OCP E4M3, "e4m3fn": max 448, no infinities) dense forward.
  * boostr, src/ops/traits/attention/flash.rs,
  * FlashAttentionOps::flash_attention_fwd_fp8 (per-tensor scales, FP32

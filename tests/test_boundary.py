@@ -37,7 +37,8 @@ def err(lib):
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("varlen_attention_fwd", "flash_attention_fwd", "flash_attention_fwd_fp8",
-              "varlen_attention_bwd", "flash_attention_bwd", "vlgqa_last_error",
+              "varlen_attention_bwd", "flash_attention_bwd", "flash_attention_decode",
+              "vlgqa_decode_workspace_floats", "vlgqa_last_error",
               "vlgqa_version"):
         assert n in names
 
@@ -268,3 +269,44 @@ def test_unpack_and_cu_seqlens_reject(lib):
     # nothing to move: OK without pointers
     assert lib.vlgqa_pack(0, 0, 0, 512, 256, 0, 0, None) == _lib.VLGQA_OK
     assert lib.vlgqa_unpack(0, A, 3, 0, 256, 0, None) == _lib.VLGQA_OK
+
+
+def decode(lib, **kw):
+    a = dict(q=A, k=A, v=A, b=16, h=32, hkv=8, sq=1, cap=16384, d=128, causal=1, w=0, n=8192,
+             dtype=BF16, out=A, lse=A, ws=A, wsf=1 << 40)
+    a.update(kw)
+    return lib.flash_attention_decode(a["q"], a["k"], a["v"], a["b"], a["h"], a["hkv"], a["sq"],
+                                      a["cap"], a["d"], a["causal"], a["w"], a["n"], a["dtype"],
+                                      a["out"], a["lse"], a["ws"], a["wsf"], None)
+
+
+@pytest.mark.parametrize("kw,code,arg", [
+    (dict(sq=9), EINVAL, "seqlen_q"),           # 9 * 4 query rows > 32
+    (dict(h=64, hkv=1), EINVAL, "seqlen_q"),
+    (dict(n=16385), EINVAL, "kv_seq_len"),
+    (dict(w=-1), EINVAL, "window_size"),
+    (dict(dtype=F32), EUNSUP, "dtype"),
+    (dict(d=96), EUNSUP, "head_dim"),
+    (dict(h=32, hkv=5), EINVAL, "num_heads"),
+    (dict(wsf=100), EINVAL, "workspace_floats"),
+    (dict(ws=0), EINVAL, "workspace"),
+    (dict(ws=MIS), EINVAL, "workspace"),
+    (dict(k=0), EINVAL, "k"),
+    (dict(causal=3), EINVAL, "causal"),
+])
+def test_decode_rejects(lib, kw, code, arg):
+    assert decode(lib, **kw) == code
+    assert err(lib).startswith(arg + ":"), err(lib)
+
+
+def test_decode_empty_problems_and_workspace_size(lib):
+    assert decode(lib, b=0, q=0, k=0, v=0, out=0, lse=0, ws=0, wsf=0) == _lib.VLGQA_OK
+    assert decode(lib, sq=0, q=0, k=0, v=0, out=0, lse=0, ws=0, wsf=0) == _lib.VLGQA_OK
+    f = lib.vlgqa_decode_workspace_floats
+    assert f(-1, 8, 128, 100) == -1
+    # one partial of 32 rows x (D + 2) floats per (batch, kv head, key slice);
+    # the size never decreases as the attended length grows
+    sizes = [f(16, 8, 128, n) for n in range(0, 20000, 97)]
+    assert all(s % (16 * 8 * 32 * 130) == 0 and s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    assert decode(lib, wsf=f(16, 8, 128, 8192) - 1) == EINVAL

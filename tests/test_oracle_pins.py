@@ -16,7 +16,7 @@ import torch
 import oracle
 from oracle import brute, e4m3, online
 from variable_length_gqa_amd import workloads as W
-from variable_length_gqa_amd.flops import visible_pairs
+from variable_length_gqa_amd.flops import visible_key_span, visible_pairs
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -407,3 +407,11 @@ def test_visible_pairs_equals_mask_count():
         for causal, window in MODES:
             m = oracle.allowed_keys(np.arange(Lq), Lq, Lk, causal, window)
             assert visible_pairs(Lq, Lk, causal, window) == int(m.sum())
+
+
+def test_visible_key_span_equals_mask_columns():
+    # keys seen by at least one row: the K/V rows a decode pass has to read
+    for (Lq, Lk) in [(1, 9), (4, 9), (9, 5), (13, 13), (1, 1), (3, 0), (0, 3)]:
+        for causal, window in MODES + [(True, 1), (False, 2)]:
+            m = oracle.allowed_keys(np.arange(Lq), Lq, Lk, causal, window)
+            assert visible_key_span(Lq, Lk, causal, window) == int(m.any(axis=0).sum())

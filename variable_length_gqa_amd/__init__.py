@@ -4,6 +4,7 @@ Entry points (HIP kernels for gfx950 behind a C ABI, see include/vlgqa.h):
   varlen_attention_fwd     packed [total, H, D] with I32 cu_seqlens, GQA, causal
   flash_attention_fwd      dense [B, H, S, D], KV capacity stride, sliding window
   flash_attention_fwd_fp8  dense OCP E4M3 with per-tensor scales
+  flash_attention_decode   dense, few queries against a long KV cache (split-KV)
       -> (output, logsumexp)
   varlen_attention_bwd     gradients of the packed forward
   flash_attention_bwd      gradients of the dense forward
@@ -13,7 +14,9 @@ Entry points (HIP kernels for gfx950 behind a C ABI, see include/vlgqa.h):
 """
 
 from .attention import (  # noqa: F401
+    decode_workspace_floats,
     flash_attention_bwd,
+    flash_attention_decode,
     flash_attention_fwd,
     flash_attention_fwd_fp8,
     varlen_attention_bwd,

@@ -22,6 +22,9 @@ SIGNATURES = {
                                  _I, _P, _P, _P]),
     "flash_attention_fwd_fp8": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I, _F, _F,
                                      _F, _F, _P, _P, _P]),
+    "flash_attention_decode": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I, _I64,
+                                    _I64, _I, _P, _P, _P, _I64, _P]),
+    "vlgqa_decode_workspace_floats": (_I64, [_I64, _I64, _I64, _I64]),
     "varlen_attention_bwd": (_I, [_P] * 8 + [_I64] * 8 + [_I, _I] + [_P] * 5),
     "flash_attention_bwd": (_I, [_P] * 6 + [_I64] * 6 + [_I, _I64, _I] + [_P] * 5),
     "vlgqa_cu_seqlens": (_I, [_P, _I64, _P, _P]),

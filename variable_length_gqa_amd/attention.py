@@ -143,6 +143,61 @@ def flash_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_h
     return out, lse
 
 
+def decode_workspace_floats(batch: int, num_kv_heads: int, head_dim: int, kv_len: int) -> int:
+    """Float32 workspace ``flash_attention_decode`` needs for ``kv_len`` attended keys."""
+    n = _lib.load().vlgqa_decode_workspace_floats(batch, num_kv_heads, head_dim, kv_len)
+    _need(n >= 0, "negative extent")
+    return int(n)
+
+
+def flash_attention_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_heads: int,
+                           num_kv_heads: int, head_dim: int, causal: bool, window_size: int = 0,
+                           kv_seq_len: int | None = None, out: torch.Tensor | None = None,
+                           lse: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None):
+    """Split-KV dense forward for decode shapes -> (out, lse), as flash_attention_fwd.
+
+    Requires S_q * num_heads / num_kv_heads <= 32.  ``workspace`` (float32, at
+    least ``decode_workspace_floats(B, Hkv, D, n)`` elements) is allocated when
+    not given; a caller decoding step by step can size one for the capacity.
+    """
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_device_tensor(name, t, dev)
+    _need(q.dtype in (torch.bfloat16, torch.float16), f"unsupported dtype {q.dtype}")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share one dtype")
+    _need(q.dim() == 4 and q.shape[1] == num_heads and q.shape[3] == head_dim,
+          "q must be [B, num_heads, S_q, head_dim]")
+    _need(k.dim() == 4 and k.shape[0] == q.shape[0] and k.shape[1] == num_kv_heads
+          and k.shape[3] == head_dim, "k must be [B, num_kv_heads, capacity, head_dim]")
+    _need(v.shape == k.shape, "v must have the shape of k")
+    B, _, Sq, _ = q.shape
+    cap = k.shape[2]
+    n = cap if kv_seq_len is None else int(kv_seq_len)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, num_heads, Sq), dtype=torch.float32, device=dev)
+    _check_device_tensor("out", out, dev)
+    _check_device_tensor("lse", lse, dev)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(lse.shape == (B, num_heads, Sq) and lse.dtype == torch.float32,
+          "lse must be float32 [B, num_heads, S_q]")
+    need = decode_workspace_floats(B, num_kv_heads, head_dim, max(n, 0))
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.float32, device=dev)
+    _check_device_tensor("workspace", workspace, dev)
+    _need(workspace.dtype == torch.float32, "workspace must be float32")
+    lib = _lib.load()
+    rc = lib.flash_attention_decode(_ptr(q), _ptr(k), _ptr(v), B, num_heads, num_kv_heads, Sq,
+                                    cap, head_dim, int(bool(causal)), int(window_size),
+                                    -1 if kv_seq_len is None else int(kv_seq_len),
+                                    _DTYPE_CODE[q.dtype], _ptr(out), _ptr(lse), _ptr(workspace),
+                                    workspace.numel(), _stream(dev))
+    _lib.check(rc)
+    return out, lse
+
+
 def flash_attention_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_heads: int,
                             num_kv_heads: int, head_dim: int, causal: bool, q_scale: float,
                             k_scale: float, v_scale: float, o_scale: float,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvlgqa.so")
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "pack.hip", "capi.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "decode.hip", "pack.hip", "capi.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

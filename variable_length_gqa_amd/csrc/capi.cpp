@@ -9,6 +9,7 @@
 #include <string>
 
 #include "bwd_params.h"
+#include "decode_params.h"
 #include "fwd_params.h"
 #include "pack_api.h"
 #include "vlgqa.h"
@@ -201,6 +202,77 @@ int flash_attention_fwd_fp8(const void* q, const void* k, const void* v, int64_t
     return fail(VLGQA_EINVAL, "q_scale", "scale products overflow or underflow f32");
   return dense_common(q, k, v, batch, num_heads, num_kv_heads, seqlen_q, seqlen_k, head_dim,
                       causal, 0, -1, vlgqa::E_E4M3, mul, omul, out, lse, hip_stream);
+}
+
+int64_t vlgqa_decode_workspace_floats(int64_t batch, int64_t num_kv_heads, int64_t head_dim,
+                                      int64_t kv_len) {
+  if (batch < 0 || num_kv_heads < 0 || head_dim < 0 || kv_len < 0) return -1;
+  return vlgqa::decode_workspace_floats(batch, num_kv_heads, head_dim, kv_len);
+}
+
+int flash_attention_decode(const void* q, const void* k, const void* v, int64_t batch,
+                           int64_t num_heads, int64_t num_kv_heads, int64_t seqlen_q,
+                           int64_t kv_capacity, int64_t head_dim, int causal, int64_t window_size,
+                           int64_t kv_seq_len, int dtype, void* out, float* lse, float* workspace,
+                           int64_t workspace_floats, void* hip_stream) {
+  g_last_error.clear();
+  int rc, elem = 0;
+  if ((rc = elem_of_dtype(dtype, &elem))) return rc;
+  if (elem == vlgqa::E_F32)
+    return fail(VLGQA_EUNSUPPORTED, "dtype", "the decode path is compiled for bf16 and f16");
+  if ((rc = check_head_dim(head_dim))) return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads))) return rc;
+  if (batch < 0) return fail(VLGQA_EINVAL, "batch", "must be non-negative");
+  if (seqlen_q < 0) return fail(VLGQA_EINVAL, "seqlen_q", "must be non-negative");
+  if (kv_capacity < 0) return fail(VLGQA_EINVAL, "kv_capacity", "must be non-negative");
+  if (window_size < 0) return fail(VLGQA_EINVAL, "window_size", "must be non-negative");
+  if (causal != 0 && causal != 1) return fail(VLGQA_EINVAL, "causal", "must be 0 or 1");
+  const int64_t group = num_heads / num_kv_heads;
+  if (seqlen_q * group > 32)
+    return fail(VLGQA_EINVAL, "seqlen_q",
+                "seqlen_q * num_heads / num_kv_heads must be at most 32 (use flash_attention_fwd)");
+  const int64_t n = kv_seq_len < 0 ? kv_capacity : kv_seq_len;
+  if (n > kv_capacity) return fail(VLGQA_EINVAL, "kv_seq_len", "exceeds the K/V buffer capacity");
+  if (kv_capacity > INT32_MAX || batch > INT32_MAX)
+    return fail(VLGQA_EINVAL, "kv_capacity", "extents must fit 32 bits");
+  if (window_size > INT32_MAX) window_size = INT32_MAX;
+  if (batch == 0 || seqlen_q == 0) return VLGQA_OK;
+  const int64_t need = vlgqa::decode_workspace_floats(batch, num_kv_heads, head_dim, n);
+  const int64_t parts = vlgqa::decode_parts(batch, num_kv_heads, head_dim, n);
+  if (batch * num_kv_heads * parts > INT32_MAX)
+    return fail(VLGQA_EINVAL, "batch", "batch * num_kv_heads too large for one launch");
+  if (workspace_floats < need)
+    return fail(VLGQA_EINVAL, "workspace_floats",
+                "smaller than vlgqa_decode_workspace_floats(batch, num_kv_heads, head_dim, n)");
+  if ((rc = check_ptr(q, "q"))) return rc;
+  if (n > 0) {
+    if ((rc = check_ptr(k, "k"))) return rc;
+    if ((rc = check_ptr(v, "v"))) return rc;
+  }
+  if ((rc = check_ptr(out, "out"))) return rc;
+  if ((rc = check_ptr(lse, "lse"))) return rc;
+  if ((rc = check_ptr(workspace, "workspace"))) return rc;
+
+  vlgqa::DecParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse; p.ws = workspace;
+  p.q_bs = num_heads * seqlen_q * head_dim; p.q_hs = seqlen_q * head_dim; p.q_rs = head_dim;
+  p.k_bs = num_kv_heads * kv_capacity * head_dim; p.k_hs = kv_capacity * head_dim;
+  p.k_rs = head_dim;
+  p.l_bs = num_heads * seqlen_q; p.l_hs = seqlen_q; p.l_rs = 1;
+  p.kv_heads = (int32_t)num_kv_heads;
+  p.group = (int32_t)group;
+  p.seqlen_q = (int32_t)seqlen_q;
+  p.kv_len = (int32_t)n;
+  p.causal = causal;
+  p.window = (int32_t)window_size;
+  p.n_bk = (int32_t)(batch * num_kv_heads);
+  p.n_parts = (int32_t)parts;
+  p.score_mul = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  p.out_mul = 1.0f;
+  hipError_t e = vlgqa::launch_decode(p, elem, (int)head_dim,
+                                      reinterpret_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
+  return VLGQA_OK;
 }
 
 static int bwd_common(vlgqa::BwdParams& p, int dtype, int64_t head_dim, int64_t rows,

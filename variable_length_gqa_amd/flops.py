@@ -43,3 +43,14 @@ def io_bytes(total_q: int, total_k: int, num_heads: int, num_kv_heads: int, head
     return (total_q * num_heads * head_dim * (elem_bytes + ob)
             + 2 * total_k * num_kv_heads * head_dim * elem_bytes
             + total_q * num_heads * 4)
+
+
+def visible_key_span(Lq: int, Lk: int, causal: bool, window: int = 0) -> int:
+    """Number of key positions visible to at least one query row: the keys a
+    pass that reads each needed K/V row once must fetch."""
+    if Lq <= 0 or Lk <= 0:
+        return 0
+    off = Lk - Lq
+    hi = min(Lk - 1, Lq - 1 + off) if (causal or window > 0) else Lk - 1
+    lo = max(0, off - window + 1) if window > 0 else 0
+    return max(0, hi - lo + 1)

@@ -175,7 +175,7 @@ def make_dense_fp8(batch, num_heads, num_kv_heads, seqlen, head_dim, causal=True
 # ---------------------------------------------------------------------------
 
 WORKLOADS = ("varlen_f32_mha", "varlen_bf16_gqa", "varlen_bf16_long", "dense_bf16_window",
-             "dense_fp8")
+             "dense_fp8", "dense_bf16_decode")
 SEEDS = {name: 1000 + i for i, name in enumerate(WORKLOADS)}
 
 
@@ -203,4 +203,9 @@ def workload(name: str):
                           window=4096, kv_seq_len=8192, capacity=16384, seed=seed, name=name)
     if name == "dense_fp8":
         return make_dense_fp8(8, 32, 8, 4096, 128, causal=True, seed=seed, name=name)
+    if name == "dense_bf16_decode":
+        # one new query per sequence against 8192 cached keys of a 16384-slot
+        # buffer (the head configuration of the dense window workload)
+        return make_dense(16, 32, 8, 1, 128, dtype=torch.bfloat16, causal=True, window=0,
+                          kv_seq_len=8192, capacity=16384, seed=seed, name=name)
     raise KeyError(name)
