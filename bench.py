@@ -50,6 +50,7 @@ KERNEL_SOURCES = {
                  "variable_length_gqa_amd/csrc/bwd_params.h",
                  "variable_length_gqa_amd/csrc/kernel_common.h"],
     "pack": ["variable_length_gqa_amd/csrc/pack.hip"],
+    "unpack": ["variable_length_gqa_amd/csrc/pack.hip"],
     "decode": ["variable_length_gqa_amd/csrc/decode.hip",
                "variable_length_gqa_amd/csrc/decode_params.h",
                "variable_length_gqa_amd/csrc/kernel_common.h"],
@@ -461,7 +462,8 @@ def bench_pack(args, dev):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic (seeded N(0,1) inputs of the workload's shapes)", "config": cfg,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload, args.which)},
         "bytes_per_step": nbytes, "copy_reference_gbs": round(copy_gbs, 1),
         "kernel_source_digest": kernel_source_digest("pack"),
     }

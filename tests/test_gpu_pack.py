@@ -78,3 +78,22 @@ def test_packed_attention_equals_padded_attention_rows():
                                        v[b:b + 1, :n].transpose(1, 2).contiguous(), H, H, D, True)
         torch.testing.assert_close(o_pad[b, :n], ob[0].transpose(0, 1), rtol=0, atol=0)
         assert torch.all(o_pad[b, n:] == 0)
+
+
+def test_debug_checks_reject_bad_offsets(monkeypatch):
+    """With the debug checks on, offsets that the kernels would trust are
+    validated on the host first (a length above max_seqlen, a wrong total)."""
+    from variable_length_gqa_amd import attention
+
+    monkeypatch.setattr(attention, "DEBUG_CHECKS", True)
+    padded = torch.zeros(2, 8, 4, 64, dtype=torch.bfloat16, device=DEV)
+    bad = torch.tensor([0, 9, 12], dtype=torch.int32, device=DEV)   # first length 9 > 8
+    with pytest.raises(ValueError, match="max_seqlen"):
+        packing.pack(padded, bad)
+    good = torch.tensor([0, 3, 8], dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="packed token count"):
+        packing.pack(padded, good, total=7)
+    with pytest.raises(ValueError, match="exceeds the packed rows"):
+        packing.unpack(torch.zeros(5, 4, 64, dtype=torch.bfloat16, device=DEV), good, 8)
+    packed = packing.pack(padded, good)
+    assert packed.shape == (8, 4, 64)

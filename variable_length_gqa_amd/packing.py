@@ -10,7 +10,8 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from .attention import _check_device_tensor, _need, _ptr, _stream
+from . import attention as _attention
+from .attention import _check_device_tensor, _need, _ptr, _stream, check_cu_seqlens
 
 
 def cu_seqlens(lengths: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -51,6 +52,8 @@ def pack(padded: torch.Tensor, cu_seqlens_: torch.Tensor, total: int | None = No
           "cu_seqlens must be int32 [B+1]")
     if total is None:
         total = int(cu_seqlens_[-1].item())
+    if _attention.DEBUG_CHECKS:
+        check_cu_seqlens(cu_seqlens_, total, S, "cu_seqlens")
     if out is None:
         out = torch.empty((total,) + tuple(padded.shape[2:]), dtype=padded.dtype, device=dev)
     _check_device_tensor("out", out, dev)
@@ -72,6 +75,10 @@ def unpack(packed: torch.Tensor, cu_seqlens_: torch.Tensor, max_seqlen: int,
     _need(cu_seqlens_.dtype == torch.int32 and cu_seqlens_.dim() == 1,
           "cu_seqlens must be int32 [B+1]")
     B = cu_seqlens_.shape[0] - 1
+    if _attention.DEBUG_CHECKS:
+        total = int(cu_seqlens_[-1].item())
+        _need(total <= packed.shape[0], f"cu_seqlens[-1] = {total} exceeds the packed rows")
+        check_cu_seqlens(cu_seqlens_, total, max_seqlen, "cu_seqlens")
     shape = (B, max_seqlen) + tuple(packed.shape[1:])
     if out is None:
         out = torch.empty(shape, dtype=packed.dtype, device=dev)
