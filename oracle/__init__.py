@@ -26,7 +26,7 @@ Modules:
   online     -- the tiled online-softmax recurrence (realizar IMP-111b) in f64.
   e4m3       -- OCP FP8 E4M3 ("fn") decode and round-to-nearest-even encode.
   backward   -- the gradient of the forward definition (dq, dk, dv), summed
-                over the query heads of a GQA group for dk/dv.
+                over the query heads of a GQA group for dk/dv; its FP8 form.
   pack       -- padded [B, S, ...] <-> packed [total, ...] by cu_seqlens.
 
 Parity pins for every function live in ``tests/test_oracle_pins.py``; none of
@@ -44,5 +44,6 @@ from .attention import (  # noqa: F401
     dense_rows,
     fp8_rows,
 )
-from .backward import attend_rows_bwd, varlen_attention_bwd, flash_attention_bwd  # noqa: F401
+from .backward import (attend_rows_bwd, varlen_attention_bwd, flash_attention_bwd,  # noqa: F401
+                       flash_attention_bwd_fp8)
 from . import brute, online, e4m3, pack  # noqa: F401
