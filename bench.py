@@ -171,10 +171,41 @@ def make_step_bwd(name, dev):
         cfg = {"workload": name, "pass": "backward", "layout": "packed varlen",
                "lengths": x.lengths_q, "total_tokens": sum(x.lengths_q), "heads": x.num_heads,
                "kv_heads": x.num_kv_heads, "head_dim": x.head_dim, "causal": x.causal}
+    elif x.scales:
+        # E4M3: O (codes) and LSE from the GPU FP8 forward, dout quantised from
+        # N(0,1) draws; the gradient scales only set the codes' range
+        dd = x.to(dev)
+        B, H, Sq, D = x.q.shape
+        sc = x.scales
+        o_scale = _fp8_o_scale()
+        out, lse = vg.flash_attention_fwd_fp8(dd.q, dd.k, dd.v, H, x.num_kv_heads, D, x.causal,
+                                              sc["q_scale"], sc["k_scale"], sc["v_scale"],
+                                              o_scale)
+        do8, do_scale = W.quantize_e4m3(W.make_dout(torch.empty(x.q.shape), 400))
+        do8 = do8.to(dev)
+        dq, dk, dv = torch.empty_like(dd.q), torch.empty_like(dd.k), torch.empty_like(dd.v)
+        ws = torch.empty(vg.attention.bwd_workspace_floats(B * Sq, B * x.k.shape[2], H,
+                                                            x.num_kv_heads, D, e4m3=True),
+                         dtype=torch.float32, device=dev)
+        gs = 1e-3
+
+        def step():
+            vg.flash_attention_bwd_fp8(do8, dd.q, dd.k, dd.v, out, lse, H, x.num_kv_heads, D,
+                                       x.causal, sc["q_scale"], sc["k_scale"], sc["v_scale"],
+                                       do_scale, o_scale, gs, gs, gs, dq=dq, dk=dk, dv=dv,
+                                       workspace=ws)
+
+        n = x.k.shape[2]
+        flops = 2.5 * F.attention_flops([Sq] * B, [n] * B, H, D, x.causal)
+        cfg = {"workload": name, "pass": "backward", "layout": "dense", "batch": B,
+               "seqlen_q": Sq, "seqlen_k": n, "heads": H, "kv_heads": x.num_kv_heads,
+               "head_dim": D, "causal": x.causal, "inputs": "E4M3 codes, per-tensor scales",
+               "outputs": "E4M3 codes", "products": "bf16 matrix cores (exact widening)"}
+        return x, step, int(flops), None, cfg, "bf16"
     else:
-        if x.scales or x.kv_seq_len not in (None, x.k.shape[2]):
-            raise SystemExit("the backward pass runs on bf16 / f16 workloads without a "
-                             "kv_seq_len shorter than the K/V buffer")
+        if x.kv_seq_len not in (None, x.k.shape[2]):
+            raise SystemExit("the backward pass runs on workloads without a kv_seq_len "
+                             "shorter than the K/V buffer")
         dd = x.to(dev)
         B, H, Sq, D = x.q.shape
         out, lse = vg.flash_attention_fwd(dd.q, dd.k, dd.v, H, x.num_kv_heads, D, x.causal,
@@ -281,6 +312,20 @@ def cpu_baseline_bwd(name, x, n_heads, unit_scale):
         oracle.varlen_attention_bwd(dO, x.q, x.k, x.v, x.cu_q, x.cu_k, x.num_heads,
                                     x.num_kv_heads, x.causal, workers=workers, heads=heads)
         fl = 2.5 * F.attention_flops(x.lengths_q, x.lengths_k, n_heads, x.head_dim, x.causal)
+    elif x.scales:
+        import torch
+
+        B, H, Sq, D = x.q.shape
+        sc = x.scales
+        do8, do_scale = W.quantize_e4m3(W.make_dout(torch.empty(x.q.shape), 400))
+        # the work does not depend on the stored output's values: q's codes
+        # stand in for them
+        # (first batch entry only: the f64 oracle needs ~4 s per head of it)
+        oracle.flash_attention_bwd_fp8(do8[:1], x.q[:1], x.k[:1], x.v[:1], x.q[:1], H,
+                                       x.num_kv_heads, x.causal, sc["q_scale"], sc["k_scale"],
+                                       sc["v_scale"], do_scale, sc["v_scale"], 1.0, 1.0, 1.0,
+                                       workers=workers, heads=heads)
+        fl = 2.5 * F.attention_flops([Sq], [x.k.shape[2]], n_heads, D, x.causal)
     else:
         B, H, Sq, D = x.q.shape
         oracle.flash_attention_bwd(dO, x.q, x.k, x.v, H, x.num_kv_heads, x.causal, x.window,
@@ -288,10 +333,11 @@ def cpu_baseline_bwd(name, x, n_heads, unit_scale):
         fl = 2.5 * F.attention_flops([Sq] * B, [x.k.shape[2]] * B, n_heads, D, x.causal,
                                      x.window)
     secs = time.perf_counter() - t0
+    which = "of batch entry 0" if x.scales else "of every sequence"
     return secs, {"value": fl / secs / unit_scale, "unit": "TFLOP/s", "cores": workers,
                   "kind": "oracle",
-                  "sample": f"backward of query heads 0..{n_heads - 1} of {x.num_heads} of every "
-                            f"sequence ({fl:.3e} algorithmic FLOPs, {secs:.1f} s wall, f64 "
+                  "sample": f"backward of query heads 0..{n_heads - 1} of {x.num_heads} {which} "
+                            f"({fl:.3e} algorithmic FLOPs, {secs:.1f} s wall, f64 "
                             f"NumPy, one process per core, masked scores computed too)"}
 
 

@@ -183,12 +183,13 @@ int flash_attention_fwd_fp8(const void* q, const void* k, const void* v,
  * not compiled: EUNSUPPORTED); f32 accumulation, gradients stored in dtype.
  *
  * workspace: caller-allocated float32 scratch, 16-byte aligned, of
- *     2 * rows * num_heads + 4 * keys * num_kv_heads * head_dim   floats,
- * rows = total_q, keys = total_k (packed) or rows = batch * seqlen_q, keys =
- * batch * seqlen_k (dense).  On return its first part holds LSE * log2(e)
- * (+inf for rows with no visible key) and then delta, head-major
- * ([num_heads][total_q], dense [batch][num_heads][seqlen_q]); the rest holds
- * f32 partial sums of dk and dv.  It is required whenever the call has work.
+ *     vlgqa_bwd_workspace_floats(rows, keys, num_heads, num_kv_heads, head_dim, 0)
+ *   = round_up(2 * rows * num_heads, 4) + 4 * keys * num_kv_heads * head_dim
+ * floats, rows = total_q, keys = total_k (packed) or rows = batch * seqlen_q,
+ * keys = batch * seqlen_k (dense).  On return its first part holds
+ * LSE * log2(e) (+inf for rows with no visible key) and then delta,
+ * head-major ([num_heads][total_q], dense [batch][num_heads][seqlen_q]); the
+ * rest holds f32 partial sums of dk and dv.  It is required whenever the call has work.
  * Calls that share a workspace on one stream are ordered by the stream;
  * concurrent calls need separate workspaces.
  * dq, dk, dv are written in full (zero for rows / keys that take part in no
@@ -237,6 +238,51 @@ int flash_attention_bwd(const void* dout, const void* q, const void* k, const vo
                         int64_t seqlen_q, int64_t seqlen_k, int64_t head_dim,
                         int causal, int64_t window_size, int dtype,
                         void* dq, void* dk, void* dv, float* workspace, void* hip_stream);
+
+/*
+ * FP8 (OCP E4M3) dense backward.  boostr, src/ops/traits/attention/flash.rs,
+ * FlashAttentionOps::flash_attention_bwd_fp8 (per-tensor dequantisation scales
+ * for the inputs and for the forward output, which serves the preprocessing
+ * step; quantisation scales for the gradients).
+ *
+ *   dout, out, q  [batch, num_heads, seqlen_q, head_dim]      uint8 E4M3 codes
+ *   k, v          [batch, num_kv_heads, seqlen_k, head_dim]   uint8 E4M3 codes
+ *   lse           [batch, num_heads, seqlen_q]                float32, natural
+ *                 log, over the scaled scores (flash_attention_fwd_fp8's lse)
+ *   q/k/v/do/o_scale  real value = code value * scale
+ *   dq/dk/dv_scale    gradient codes = E4M3(g / scale), round to nearest even,
+ *                     saturating at +-448
+ *   dq [.., seqlen_q, ..], dk, dv [.., seqlen_k, ..]          uint8 E4M3 codes
+ *
+ * The gradients are those of flash_attention_bwd on the dequantised inputs
+ * (scale 1/sqrt(head_dim); causal or no mask: this method takes no window),
+ * with delta_i = dout_i . out_i taken from the stored output.  f32
+ * accumulation; P and dS are rounded to bf16 before the products that use
+ * them.
+ *
+ * workspace: float32, 16-byte aligned, workspace_floats >=
+ * vlgqa_bwd_workspace_floats(batch * seqlen_q, batch * seqlen_k, num_heads,
+ * num_kv_heads, head_dim, 1): the 16-bit layout followed by bf16 copies of the
+ * codes of q, dout, k and v.  Contents on return are unspecified.
+ *
+ * Errors: EINVAL for a scale that is not finite and positive, scale products
+ * outside the f32 range, a workspace that is too small, and as
+ * flash_attention_bwd; EUNSUPPORTED for head_dim not in {64, 128}.
+ */
+int flash_attention_bwd_fp8(const void* dout, const void* q, const void* k, const void* v,
+                            const void* out, const float* lse,
+                            int64_t batch, int64_t num_heads, int64_t num_kv_heads,
+                            int64_t seqlen_q, int64_t seqlen_k, int64_t head_dim, int causal,
+                            float q_scale, float k_scale, float v_scale, float do_scale,
+                            float o_scale, float dq_scale, float dk_scale, float dv_scale,
+                            void* dq, void* dk, void* dv, float* workspace,
+                            int64_t workspace_floats, void* hip_stream);
+
+/* Workspace floats of the backward entry points (e4m3 = 1: the FP8 form),
+ * for rows query rows and keys key rows in total (-1 for a negative
+ * argument).  Host-only arithmetic. */
+int64_t vlgqa_bwd_workspace_floats(int64_t rows, int64_t keys, int64_t num_heads,
+                                   int64_t num_kv_heads, int64_t head_dim, int e4m3);
 
 /*
  * Packing of padded batches into the varlen layout.

@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("varlen_attention_fwd", "flash_attention_fwd", "flash_attention_fwd_fp8",
               "varlen_attention_bwd", "flash_attention_bwd", "flash_attention_decode",
-              "vlgqa_decode_workspace_floats", "vlgqa_last_error",
+              "vlgqa_decode_workspace_floats", "flash_attention_bwd_fp8",
+              "vlgqa_bwd_workspace_floats", "vlgqa_last_error",
               "vlgqa_version"):
         assert n in names
 
@@ -310,3 +311,44 @@ def test_decode_empty_problems_and_workspace_size(lib):
     assert all(s % (16 * 8 * 32 * 130) == 0 and s > 0 for s in sizes)
     assert sizes == sorted(sizes)
     assert decode(lib, wsf=f(16, 8, 128, 8192) - 1) == EINVAL
+
+
+def bwd8(lib, **kw):
+    a = dict(do=A, q=A, k=A, v=A, o=A, lse=A, b=8, h=32, hkv=8, sq=4096, sk=4096, d=128,
+             causal=1, qs=0.01, ks=0.01, vs=0.01, dos=0.01, os=0.01, dqs=0.01, dks=0.01,
+             dvs=0.01, dq=A, dk=A, dv=A, ws=A, wsf=1 << 40)
+    a.update(kw)
+    return lib.flash_attention_bwd_fp8(a["do"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["b"],
+                                       a["h"], a["hkv"], a["sq"], a["sk"], a["d"], a["causal"],
+                                       a["qs"], a["ks"], a["vs"], a["dos"], a["os"], a["dqs"],
+                                       a["dks"], a["dvs"], a["dq"], a["dk"], a["dv"], a["ws"],
+                                       a["wsf"], None)
+
+
+@pytest.mark.parametrize("kw,code,arg", [
+    (dict(qs=0.0), EINVAL, "q_scale"), (dict(dos=-1.0), EINVAL, "do_scale"),
+    (dict(os=float("nan")), EINVAL, "o_scale"), (dict(dqs=float("inf")), EINVAL, "dq_scale"),
+    (dict(dks=0.0), EINVAL, "dk_scale"), (dict(dvs=-2.0), EINVAL, "dv_scale"),
+    (dict(qs=1e-30, ks=1e-30), EINVAL, "q_scale"),
+    (dict(d=96), EUNSUP, "head_dim"), (dict(h=32, hkv=5), EINVAL, "num_heads"),
+    (dict(sq=-1), EINVAL, "seqlen_q"), (dict(causal=2), EINVAL, "causal"),
+    (dict(wsf=1000), EINVAL, "workspace_floats"), (dict(ws=MIS), EINVAL, "workspace"),
+    (dict(k=0), EINVAL, "k"), (dict(q=MIS), EINVAL, "q"), (dict(dout=0), EINVAL, "dout"),
+])
+def test_bwd_fp8_rejects(lib, kw, code, arg):
+    if "dout" in kw:
+        kw = dict(do=kw.pop("dout"))
+    assert bwd8(lib, **kw) == code
+    assert err(lib).startswith(arg + ":"), err(lib)
+
+
+def test_bwd_workspace_sizes(lib):
+    f = lib.vlgqa_bwd_workspace_floats
+    assert f(-1, 1, 1, 1, 64, 0) == -1
+    # row planes rounded up to 16 bytes, then 4 D floats per key and kv head
+    assert f(3, 5, 1, 1, 64, 0) == 8 + 4 * 5 * 64
+    assert f(4, 5, 2, 1, 64, 0) == 16 + 4 * 5 * 64
+    # E4M3: plus bf16 copies of q and dout (rows x heads) and k and v (keys x kv heads)
+    assert f(4, 5, 2, 1, 64, 1) == 16 + 4 * 5 * 64 + (4 * 2 + 5 * 1) * 64
+    assert bwd8(lib, b=0, q=0, k=0, v=0, o=0, lse=0, dq=0, dk=0, dv=0, ws=0, wsf=0) == \
+        _lib.VLGQA_OK

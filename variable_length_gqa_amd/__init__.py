@@ -8,6 +8,7 @@ Entry points (HIP kernels for gfx950 behind a C ABI, see include/vlgqa.h):
       -> (output, logsumexp)
   varlen_attention_bwd     gradients of the packed forward
   flash_attention_bwd      gradients of the dense forward
+  flash_attention_bwd_fp8  gradients of the E4M3 forward, as E4M3 codes
       -> (dq, dk, dv)
   packing.cu_seqlens / packing.pack / packing.unpack
                            lengths -> cu_seqlens, padded <-> packed on the device
@@ -16,6 +17,7 @@ Entry points (HIP kernels for gfx950 behind a C ABI, see include/vlgqa.h):
 from .attention import (  # noqa: F401
     decode_workspace_floats,
     flash_attention_bwd,
+    flash_attention_bwd_fp8,
     flash_attention_decode,
     flash_attention_fwd,
     flash_attention_fwd_fp8,

@@ -27,6 +27,9 @@ SIGNATURES = {
     "vlgqa_decode_workspace_floats": (_I64, [_I64, _I64, _I64, _I64]),
     "varlen_attention_bwd": (_I, [_P] * 8 + [_I64] * 8 + [_I, _I] + [_P] * 5),
     "flash_attention_bwd": (_I, [_P] * 6 + [_I64] * 6 + [_I, _I64, _I] + [_P] * 5),
+    "flash_attention_bwd_fp8": (_I, [_P] * 6 + [_I64] * 6 + [_I] + [_F] * 8 + [_P] * 4 +
+                                [_I64, _P]),
+    "vlgqa_bwd_workspace_floats": (_I64, [_I64] * 5 + [_I]),
     "vlgqa_cu_seqlens": (_I, [_P, _I64, _P, _P]),
     "vlgqa_pack": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P]),
     "vlgqa_unpack": (_I, [_P, _P, _I64, _I64, _I64, _P, _P]),

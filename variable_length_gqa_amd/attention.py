@@ -11,7 +11,8 @@ Argument order follows the pages' signatures:
     ``FlashAttentionOps::flash_attention_fwd`` / ``flash_attention_fwd_fp8``
 The forwards return ``(output, logsumexp)``; the backwards
 (``VarLenAttentionOps::varlen_attention_bwd``,
-``FlashAttentionOps::flash_attention_bwd``) return ``(dq, dk, dv)``.
+``FlashAttentionOps::flash_attention_bwd`` / ``flash_attention_bwd_fp8``)
+return ``(dq, dk, dv)``.
 """
 
 from __future__ import annotations
@@ -251,9 +252,12 @@ def _check_bwd_common(dout, q, k, v, out, lse, dev):
 
 
 def bwd_workspace_floats(rows: int, keys: int, num_heads: int, num_kv_heads: int,
-                         head_dim: int) -> int:
-    """float32 elements of the backward workspace (see include/vlgqa.h)."""
-    return 2 * rows * num_heads + 4 * keys * num_kv_heads * head_dim
+                         head_dim: int, e4m3: bool = False) -> int:
+    """float32 elements of the backward workspace (the library's own count)."""
+    n = _lib.load().vlgqa_bwd_workspace_floats(rows, keys, num_heads, num_kv_heads, head_dim,
+                                               int(bool(e4m3)))
+    _need(n >= 0, "negative extent")
+    return int(n)
 
 
 def _bwd_outputs(q, k, v, dq, dk, dv, ws, ws_floats, dev):
@@ -344,5 +348,49 @@ def flash_attention_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v:
                                  B, num_heads, num_kv_heads, Sq, Sk, head_dim,
                                  int(bool(causal)), int(window_size), _DTYPE_CODE[q.dtype],
                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), _stream(dev))
+    _lib.check(rc)
+    return dq, dk, dv
+
+
+def flash_attention_bwd_fp8(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                            v: torch.Tensor, output: torch.Tensor, lse: torch.Tensor,
+                            num_heads: int, num_kv_heads: int, head_dim: int, causal: bool,
+                            q_scale: float, k_scale: float, v_scale: float, do_scale: float,
+                            o_scale: float, dq_scale: float, dk_scale: float, dv_scale: float,
+                            dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                            dv: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None):
+    """FP8 (E4M3 codes as uint8) dense backward -> (dq8, dk8, dv8) uint8 codes.
+
+    Inputs are codes with dequantisation scales (real = code * scale); the
+    gradients come back as E4M3(g / g_scale).  ``lse`` is the FP8 forward's.
+    """
+    dev = q.device
+    for name, t in (("dout", dout), ("q", q), ("k", k), ("v", v), ("output", output),
+                    ("lse", lse)):
+        _check_device_tensor(name, t, dev)
+    for name, t in (("dout", dout), ("q", q), ("k", k), ("v", v), ("output", output)):
+        _need(t.dtype == torch.uint8, f"{name} must hold E4M3 codes as uint8")
+    _need(q.dim() == 4 and q.shape[1] == num_heads and q.shape[3] == head_dim,
+          "q must be [B, num_heads, S_q, head_dim]")
+    _need(k.dim() == 4 and k.shape[0] == q.shape[0] and k.shape[1] == num_kv_heads
+          and k.shape[3] == head_dim, "k must be [B, num_kv_heads, S_k, head_dim]")
+    _need(v.shape == k.shape, "v must have the shape of k")
+    _need(dout.shape == q.shape and output.shape == q.shape,
+          "dout and output must have the shape of q")
+    B, _, Sq, _ = q.shape
+    Sk = k.shape[2]
+    _need(lse.dtype == torch.float32 and lse.shape == (B, num_heads, Sq),
+          "lse must be float32 [B, num_heads, S_q]")
+    ws_floats = bwd_workspace_floats(B * Sq, B * Sk, num_heads, num_kv_heads, head_dim, True)
+    dq, dk, dv, ws = _bwd_outputs(q, k, v, dq, dk, dv, workspace, ws_floats, dev)
+    lib = _lib.load()
+    rc = lib.flash_attention_bwd_fp8(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(output),
+                                     _ptr(lse), B, num_heads, num_kv_heads, Sq, Sk, head_dim,
+                                     int(bool(causal)), float(q_scale), float(k_scale),
+                                     float(v_scale), float(do_scale), float(o_scale),
+                                     float(dq_scale), float(dk_scale), float(dv_scale),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                     _stream(dev))
     _lib.check(rc)
     return dq, dk, dv

@@ -1,5 +1,6 @@
 // Fused attention backward for gfx950 (CDNA4): packed varlen and dense layouts,
-// GQA, causal / sliding-window masks, bf16 / f16 storage, f32 accumulation.
+// GQA, causal / sliding-window masks, bf16 / f16 / E4M3 storage, f32
+// accumulation.
 //
 // What is computed (the gradient of the forward, for the interface of boostr
 // varlen_attention.rs ``varlen_attention_bwd`` and boostr flash.rs
@@ -11,7 +12,7 @@
 //   dq_i  = scale sum_j dS_ij k_j,       dk_j = scale sum_i dS_ij q_i
 // with dk / dv of a kv head summed over its G query heads.
 //
-// Four launches:
+// Four launches (five with the dK / dV reduction, more for E4M3 inputs):
 //   bwd_rowsum_kernel  delta_i = dO_i.O_i and LSE_i log2(e) per (row, head),
 //                      written head-major into the caller's workspace (so a
 //                      query tile's values are contiguous).
@@ -36,6 +37,17 @@
 // In dQ the lane owns a query:
 //   S^T = K Q^T, dP^T = V dO^T   A = K / V rows (LDS), B = Q^T / dO^T (registers)
 //   dQ^T += K^T dS^T             A = K^T by transposing LDS reads, B = dS^T
+//
+// E4M3 inputs (boostr flash.rs ``flash_attention_bwd_fp8``: per-tensor
+// dequantisation scales for q, k, v, dout and the forward output, quantisation
+// scales for dq, dk, dv): the codes of q, k, v and dout are first widened to
+// bf16 (exact: every E4M3 value is a bf16 value) into the workspace, and the
+// same kernels run on those copies with the scales folded into their
+// multipliers: scores q_scale k_scale / sqrt(D), dP do_scale v_scale, delta
+// do_scale o_scale (taken from the codes of dout and of the output), stored
+// gradients dq k_scale / (sqrt(D) dq_scale), dk q_scale / (sqrt(D) dk_scale),
+// dv do_scale / dv_scale, encoded as E4M3 with round to nearest even,
+// saturating at +-448.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -61,6 +73,14 @@ __device__ __forceinline__ float hi16(uint32_t w) {
   } else {
     return __uint_as_float(w & 0xFFFF0000u);
   }
+}
+
+// two E4M3 codes (bytes 0-1 or 2-3 of w) -> two bf16 values, exact
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Workspace layout (f32): [2][B][H][rows]: plane 0 = LSE * log2(e) (+inf for a
@@ -111,6 +131,59 @@ __global__ __launch_bounds__(256) void bwd_rowsum_kernel(BwdParams p) {
     p.delta[wi] = lse == -INFINITY ? INFINITY : lse * kLog2e;
     p.delta[ws_plane(p) + wi] = acc;
   }
+}
+
+// E4M3 form: D/16 lanes per (row, head), 16 codes of dO and of O each;
+// delta = do_scale o_scale sum(dO8 O8)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowsum8_kernel(BwdParams p) {
+  constexpr int LPR = D / 16;
+  constexpr int PPW = 64 / LPR;
+  const int64_t npairs = (int64_t)p.d_batch * p.d_rows * p.heads;
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * PPW + lane / LPR;
+  const int sub = lane % LPR;
+  float acc = 0.0f;
+  int h = 0, b = 0;
+  int64_t r = 0;
+  if (pair < npairs) {
+    h = (int)(pair % p.heads);
+    const int64_t rest = pair / p.heads;
+    r = rest % p.d_rows;
+    b = (int)(rest / p.d_rows);
+    const int64_t off = (int64_t)b * p.q_bs + r * p.q_rs + (int64_t)h * p.q_hs + sub * 16;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.do8) + off);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.o) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const uint32_t x = e4m3x2_to_bf16x2(a[i], hi), y = e4m3x2_to_bf16x2(c[i], hi);
+        acc += lo16<E_BF16>(x) * lo16<E_BF16>(y) + hi16<E_BF16>(x) * hi16<E_BF16>(y);
+      }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (pair < npairs && sub == 0) {
+    const float lse = p.lse[(int64_t)b * p.l_bs + r * p.l_rs + (int64_t)h * p.l_hs];
+    const int64_t wi = ws_index(p, b, r, h);
+    p.delta[wi] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    p.delta[ws_plane(p) + wi] = acc * p.delta_mul;
+  }
+}
+
+// E4M3 codes -> bf16 copy, 16 codes per thread (n16 = elements / 16)
+__global__ __launch_bounds__(256) void widen_e4m3_kernel(const uint8_t* __restrict__ src,
+                                                         uint16_t* __restrict__ dst, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const u32x4 c = *reinterpret_cast<const u32x4*>(src + i * 16);
+  const u32x4 lo = {e4m3x2_to_bf16x2(c[0], false), e4m3x2_to_bf16x2(c[0], true),
+                    e4m3x2_to_bf16x2(c[1], false), e4m3x2_to_bf16x2(c[1], true)};
+  const u32x4 hi = {e4m3x2_to_bf16x2(c[2], false), e4m3x2_to_bf16x2(c[2], true),
+                    e4m3x2_to_bf16x2(c[3], false), e4m3x2_to_bf16x2(c[3], true)};
+  *reinterpret_cast<u32x4*>(dst + i * 16) = lo;
+  *reinterpret_cast<u32x4*>(dst + i * 16 + 8) = hi;
 }
 
 // ---------------------------------------------------------------------------
@@ -207,6 +280,22 @@ __device__ __forceinline__ void store_rows(void* base, int64_t row_off, int hl,
   }
 }
 
+// the same as E4M3 codes (round to nearest even, saturating at +-448)
+template <int D>
+__device__ __forceinline__ void store_rows_e4m3(void* base, int64_t row_off, int hl,
+                                                const f32x16 (&acc)[D / 32], float mul) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + g * 8 + 4 * hl;
+      const uint32_t v = pack4_fp8(sat448(acc[db][4 * g + 0] * mul), sat448(acc[db][4 * g + 1] * mul),
+                                   sat448(acc[db][4 * g + 2] * mul), sat448(acc[db][4 * g + 3] * mul));
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(base) + row_off + d0) = v;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK and dV
 // ---------------------------------------------------------------------------
@@ -255,6 +344,7 @@ void bwd_kv_kernel(BwdParams p) {
   const int off = sb.Lk - sb.Lq;
   const bool upper = p.causal || p.window > 0;
   const float mul = p.score_mul;
+  const float dpm = p.dp_mul;
 
   // K^T (and for dK V^T) fragments of the lane's key: k[key][16 ks + 8 hl .. +8]
   u32x4 kf[C::NS], vf[MODE == MODE_DK ? C::NS : 1];
@@ -379,7 +469,8 @@ void bwd_kv_kernel(BwdParams p) {
           if constexpr (MODE == MODE_DV)
             bk[t2][i] = pack2<ELEM>(p0, p1);
           else
-            bk[t2][i] = pack2<ELEM>(p0 * (dp[r] - dl[j][e]), p1 * (dp[r + 1] - dl[j][e + 1]));
+            bk[t2][i] = pack2<ELEM>(p0 * __builtin_fmaf(dp[r], dpm, -dl[j][e]),
+                                    p1 * __builtin_fmaf(dp[r + 1], dpm, -dl[j][e + 1]));
         }
       }
       // dV^T += dO^T P  or  dK^T += Q^T dS  (A by transposing reads)
@@ -398,13 +489,13 @@ void bwd_kv_kernel(BwdParams p) {
   }
 
   if (key < sb.Lk) {
-    if (p.n_split == 1) {
+    if (p.n_split == 1 && !p.e4m3) {
       const int64_t row = (int64_t)b * p.k_bs + (int64_t)(sb.k_start + key) * p.k_rs +
                           (int64_t)kvh * p.k_hs;
       if constexpr (MODE == MODE_DV)
-        store_rows<ELEM, D>(p.dv, row, hl, acc, 1.0f);
+        store_rows<ELEM, D>(p.dv, row, hl, acc, p.dv_mul);
       else
-        store_rows<ELEM, D>(p.dk, row, hl, acc, p.scale);
+        store_rows<ELEM, D>(p.dk, row, hl, acc, p.dk_mul);
     } else {
       // f32 partial of this split: [mode][sp][kp_row][kvh][d]
       const int64_t kp = (p.cu_k ? 0 : (int64_t)b * p.seqlen_k) + sb.k_start + key;
@@ -422,8 +513,9 @@ void bwd_kv_kernel(BwdParams p) {
   }
 }
 
-// Sum the n_split partials of dK (times scale) and dV and store them in the
-// input dtype: one thread per (key row, kv head, 8 d).
+// Sum the n_split partials of dK and dV, apply their multipliers and store
+// them in the input dtype, or as E4M3 codes: one thread per (key row, kv head,
+// 8 d).
 template <int ELEM, int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
   const int64_t n = (int64_t)p.kp_rows * p.kv_heads * (D / 8);
@@ -453,11 +545,25 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
   const int64_t b = p.cu_k ? 0 : kp / p.seqlen_k;
   const int64_t key = p.cu_k ? kp : kp % p.seqlen_k;
   const int64_t off = b * p.k_bs + key * p.k_rs + (int64_t)kvh * p.k_hs + c * 8;
+  const float km = p.dk_mul, vm = p.dv_mul;
+  if (p.e4m3) {
+    const u32x2 ok = {pack4_fp8(sat448(sk[0] * km), sat448(sk[1] * km), sat448(sk[2] * km),
+                                sat448(sk[3] * km)),
+                      pack4_fp8(sat448(sk[4] * km), sat448(sk[5] * km), sat448(sk[6] * km),
+                                sat448(sk[7] * km))};
+    const u32x2 ov = {pack4_fp8(sat448(sv[0] * vm), sat448(sv[1] * vm), sat448(sv[2] * vm),
+                                sat448(sv[3] * vm)),
+                      pack4_fp8(sat448(sv[4] * vm), sat448(sv[5] * vm), sat448(sv[6] * vm),
+                                sat448(sv[7] * vm))};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.dk) + off) = ok;
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.dv) + off) = ov;
+    return;
+  }
   u32x4 ok, ov;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    ok[j] = pack2<ELEM>(sk[2 * j] * p.scale, sk[2 * j + 1] * p.scale);
-    ov[j] = pack2<ELEM>(sv[2 * j], sv[2 * j + 1]);
+    ok[j] = pack2<ELEM>(sk[2 * j] * km, sk[2 * j + 1] * km);
+    ov[j] = pack2<ELEM>(sv[2 * j] * vm, sv[2 * j + 1] * vm);
   }
   *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dk) + off) = ok;
   *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dv) + off) = ov;
@@ -496,6 +602,7 @@ void bwd_dq_kernel(BwdParams p) {
   const int hl = lane >> 5, ql = lane & 31;
   const int qrow = r0 + 32 * wid + ql;
   const float mul = p.score_mul;
+  const float dpm = p.dp_mul;
   const int off = sb.Lk - sb.Lq;
   const bool upper = p.causal || p.window > 0;
 
@@ -598,7 +705,8 @@ void bwd_dq_kernel(BwdParams p) {
           const int r = 8 * t2 + 2 * i;
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], mul, -lse2));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r + 1], mul, -lse2));
-          dsk[t2][i] = pack2<ELEM>(p0 * (dp[r] - dlt), p1 * (dp[r + 1] - dlt));
+          dsk[t2][i] = pack2<ELEM>(p0 * __builtin_fmaf(dp[r], dpm, -dlt),
+                                   p1 * __builtin_fmaf(dp[r + 1], dpm, -dlt));
         }
       }
 #pragma unroll
@@ -624,7 +732,10 @@ void bwd_dq_kernel(BwdParams p) {
   if (qrow < sb.Lq) {
     const int64_t row = (int64_t)b * p.q_bs + (int64_t)(sb.q_start + qrow) * p.q_rs +
                         (int64_t)h * p.q_hs;
-    store_rows<ELEM, D>(p.dq, row, hl, dq, p.scale);
+    if (p.e4m3)
+      store_rows_e4m3<D>(p.dq, row, hl, dq, p.dq_mul);
+    else
+      store_rows<ELEM, D>(p.dq, row, hl, dq, p.dq_mul);
   }
 }
 
@@ -648,21 +759,46 @@ bool plan_bwd(BwdParams& p, int head_dim) {
   return pairs / (4 * (64 / (head_dim / 8))) < INT32_MAX / 2;
 }
 
+BwdWorkspace bwd_workspace(int64_t rows, int64_t keys, int64_t heads, int64_t kv_heads,
+                           int64_t head_dim, bool e4m3) {
+  BwdWorkspace w;
+  w.part = (2 * rows * heads + 3) / 4 * 4;  // 16-byte aligned parts
+  w.wide = w.part + 4 * keys * kv_heads * head_dim;
+  w.total = w.wide + (e4m3 ? (rows * heads + keys * kv_heads) * head_dim : 0);
+  return w;
+}
+
 hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t stream) {
   const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
-  const int ppb = 4 * (64 / (head_dim / 8));
+  const int ppb = 4 * (64 / (head_dim / (p.e4m3 ? 16 : 8)));
   const int64_t nred = (int64_t)p.kp_rows * p.kv_heads * (head_dim / 8);
   const int64_t streams8 = ((int64_t)p.batch * p.kv_heads * p.n_split + 7) / 8 * 8;
   const int64_t groups8 = ((int64_t)p.n_qtiles * p.batch * p.kv_heads + 7) / 8 * 8;
   const dim3 g0((unsigned)((pairs + ppb - 1) / ppb)), g1((unsigned)(p.n_ktiles * streams8)),
       g2((unsigned)(groups8 * p.group)), g3((unsigned)((nred + 255) / 256)), blk(kThreads);
+  const bool reduce = p.n_split > 1 || p.e4m3;
+  if (p.e4m3) {
+    // bf16 copies of the codes, then the row terms from the codes of dO and O
+    const struct { const void* src; void* dst; int64_t n; } w[4] = {
+        {p.q8, p.wq, p.n_q}, {p.do8, p.wdo, p.n_q}, {p.k8, p.wk, p.n_k}, {p.v8, p.wv, p.n_k}};
+    for (const auto& t : w)
+      if (t.n > 0)
+        hipLaunchKernelGGL(widen_e4m3_kernel, dim3((unsigned)((t.n / 16 + 255) / 256)), dim3(256),
+                           0, stream, reinterpret_cast<const uint8_t*>(t.src),
+                           reinterpret_cast<uint16_t*>(t.dst), t.n / 16);
+    if (pairs > 0) {
+      if (head_dim == 128) hipLaunchKernelGGL((bwd_rowsum8_kernel<128>), g0, blk, 0, stream, p);
+      else hipLaunchKernelGGL((bwd_rowsum8_kernel<64>), g0, blk, 0, stream, p);
+    }
+  }
 #define VLGQA_BWD(E, D)                                                        \
   do {                                                                         \
-    if (pairs > 0) hipLaunchKernelGGL((bwd_rowsum_kernel<E, D>), g0, blk, 0, stream, p); \
+    if (pairs > 0 && !p.e4m3)                                                  \
+      hipLaunchKernelGGL((bwd_rowsum_kernel<E, D>), g0, blk, 0, stream, p);    \
     if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DV>), g1, blk, 0, stream, p); \
     if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DK>), g1, blk, 0, stream, p); \
     if (g2.x > 0) hipLaunchKernelGGL((bwd_dq_kernel<E, D>), g2, blk, 0, stream, p);     \
-    if (p.n_split > 1 && g3.x > 0)                                                       \
+    if (reduce && g3.x > 0)                                                              \
       hipLaunchKernelGGL((bwd_reduce_kernel<E, D>), g3, blk, 0, stream, p);              \
   } while (0)
   if (head_dim == 128 && elem == E_BF16) VLGQA_BWD(E_BF16, 128);

@@ -42,7 +42,35 @@ struct BwdParams {
   int32_t n_qtiles;   // ceil(max_seqlen_q / 128): query tiles of the dQ kernel
   float score_mul;    // log2(e) / sqrt(D): scores into the log2 domain
   float scale;        // 1 / sqrt(D)
+  // multipliers of dP = dO.V^T and of the stored dq, dk, dv (16-bit inputs:
+  // 1, 1/sqrt(D), 1/sqrt(D), 1; E4M3 inputs: the per-tensor scales folded in)
+  float dp_mul, dq_mul, dk_mul, dv_mul;
+  // E4M3 path: q, k, v, dout point at bf16 copies of the codes (exact,
+  // unscaled) made by the widening kernel from q8 .. do8; delta is taken from
+  // the codes of dout and o times delta_mul; dq, dk, dv are E4M3 codes (dk, dv
+  // always through the f32 partials)
+  int32_t e4m3;
+  float delta_mul;
+  const void* q8;
+  const void* k8;
+  const void* v8;
+  const void* do8;
+  // bf16 copies (in the workspace) and their element counts
+  void* wq;
+  void* wk;
+  void* wv;
+  void* wdo;
+  int64_t n_q, n_k;   // elements of q (= dout) and of k (= v)
 };
+
+// float32 workspace of the backward: the row planes (LSE log2 e, delta), the
+// dk / dv partials, and for E4M3 inputs the bf16 copies of q, dout, k and v;
+// returns the offsets of the parts in floats
+struct BwdWorkspace {
+  int64_t part, wide, total;
+};
+BwdWorkspace bwd_workspace(int64_t rows, int64_t keys, int64_t heads, int64_t kv_heads,
+                           int64_t head_dim, bool e4m3);
 
 bool plan_bwd(BwdParams& p, int head_dim);
 

@@ -278,7 +278,9 @@ int flash_attention_decode(const void* q, const void* k, const void* v, int64_t 
 static int bwd_common(vlgqa::BwdParams& p, int dtype, int64_t head_dim, int64_t rows,
                       void* hip_stream) {
   int rc;
-  if (dtype != VLGQA_BF16 && dtype != VLGQA_F16) {
+  if (p.e4m3) {
+    dtype = VLGQA_BF16;  // the kernels run on the bf16 copies of the codes
+  } else if (dtype != VLGQA_BF16 && dtype != VLGQA_F16) {
     if (dtype == VLGQA_F32) return fail(VLGQA_EUNSUPPORTED, "dtype", "the backward is compiled for bf16 and f16 only");
     return fail(VLGQA_EUNSUPPORTED, "dtype", "unknown dtype code");
   }
@@ -290,8 +292,14 @@ static int bwd_common(vlgqa::BwdParams& p, int dtype, int64_t head_dim, int64_t 
     if ((rc = check_ptr(p.lse, "lse"))) return rc;
     if ((rc = check_ptr(p.dq, "dq"))) return rc;
   }
-  p.score_mul = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
-  p.scale = (float)(1.0 / std::sqrt((double)head_dim));
+  if (!p.e4m3) {
+    p.score_mul = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    p.scale = (float)(1.0 / std::sqrt((double)head_dim));
+    p.dp_mul = 1.0f;
+    p.dq_mul = p.scale;
+    p.dk_mul = p.scale;
+    p.dv_mul = 1.0f;
+  }
   if (!vlgqa::plan_bwd(p, (int)head_dim))
     return fail(VLGQA_EINVAL, "max_seqlen_q", "problem too large for one launch");
   const int elem = dtype == VLGQA_F16 ? vlgqa::E_F16 : vlgqa::E_BF16;
@@ -352,7 +360,9 @@ int varlen_attention_bwd(const void* dout, const void* q, const void* k, const v
   p.max_seqlen_k = (int32_t)max_seqlen_k;
   p.d_batch = 1; p.d_rows = (int32_t)total_q;
   p.kp_rows = (int32_t)total_k;
-  p.part = workspace ? workspace + 2 * total_q * num_heads : nullptr;
+  p.part = workspace ? workspace + vlgqa::bwd_workspace(total_q, total_k, num_heads,
+                                                       num_kv_heads, head_dim, false).part
+                     : nullptr;
   return bwd_common(p, dtype, head_dim, total_q, hip_stream);
 }
 
@@ -404,8 +414,110 @@ int flash_attention_bwd(const void* dout, const void* q, const void* k, const vo
   p.d_batch = (int32_t)batch; p.d_rows = (int32_t)seqlen_q;
   if (batch * seqlen_k > INT32_MAX) return fail(VLGQA_EINVAL, "seqlen_k", "batch * seqlen_k must fit 32 bits");
   p.kp_rows = (int32_t)(batch * seqlen_k);
-  p.part = workspace ? workspace + 2 * batch * seqlen_q * num_heads : nullptr;
+  p.part = workspace ? workspace + vlgqa::bwd_workspace(batch * seqlen_q, batch * seqlen_k,
+                                                       num_heads, num_kv_heads, head_dim,
+                                                       false).part
+                     : nullptr;
   return bwd_common(p, dtype, head_dim, batch * seqlen_q, hip_stream);
+}
+
+int64_t vlgqa_bwd_workspace_floats(int64_t rows, int64_t keys, int64_t num_heads,
+                                   int64_t num_kv_heads, int64_t head_dim, int e4m3) {
+  if (rows < 0 || keys < 0 || num_heads < 0 || num_kv_heads < 0 || head_dim < 0) return -1;
+  return vlgqa::bwd_workspace(rows, keys, num_heads, num_kv_heads, head_dim, e4m3 != 0).total;
+}
+
+int flash_attention_bwd_fp8(const void* dout, const void* q, const void* k, const void* v,
+                            const void* out, const float* lse, int64_t batch, int64_t num_heads,
+                            int64_t num_kv_heads, int64_t seqlen_q, int64_t seqlen_k,
+                            int64_t head_dim, int causal, float q_scale, float k_scale,
+                            float v_scale, float do_scale, float o_scale, float dq_scale,
+                            float dk_scale, float dv_scale, void* dq, void* dk, void* dv,
+                            float* workspace, int64_t workspace_floats, void* hip_stream) {
+  g_last_error.clear();
+  int rc;
+  const struct { const char* name; float value; } scales[] = {
+      {"q_scale", q_scale},   {"k_scale", k_scale},   {"v_scale", v_scale},
+      {"do_scale", do_scale}, {"o_scale", o_scale},   {"dq_scale", dq_scale},
+      {"dk_scale", dk_scale}, {"dv_scale", dv_scale}};
+  for (const auto& s : scales)
+    if (!std::isfinite(s.value) || !(s.value > 0.0f))
+      return fail(VLGQA_EINVAL, s.name, "must be finite and positive");
+  if ((rc = check_head_dim(head_dim))) return rc;
+  if ((rc = check_heads(num_heads, num_kv_heads))) return rc;
+  if (batch < 0) return fail(VLGQA_EINVAL, "batch", "must be non-negative");
+  if (seqlen_q < 0) return fail(VLGQA_EINVAL, "seqlen_q", "must be non-negative");
+  if (seqlen_k < 0) return fail(VLGQA_EINVAL, "seqlen_k", "must be non-negative");
+  if (causal != 0 && causal != 1) return fail(VLGQA_EINVAL, "causal", "must be 0 or 1");
+  if (seqlen_q > INT32_MAX || seqlen_k > INT32_MAX || batch > INT32_MAX)
+    return fail(VLGQA_EINVAL, "seqlen_q", "extents must fit 32 bits");
+  if (batch * seqlen_k > INT32_MAX)
+    return fail(VLGQA_EINVAL, "seqlen_k", "batch * seqlen_k must fit 32 bits");
+  const double rs = 1.0 / std::sqrt((double)head_dim);
+  const double m[6] = {(double)q_scale * k_scale * 1.4426950408889634 * rs,
+                       (double)do_scale * v_scale,
+                       (double)k_scale * rs / dq_scale,
+                       (double)q_scale * rs / dk_scale,
+                       (double)do_scale / dv_scale,
+                       (double)do_scale * o_scale};
+  for (double x : m)
+    if (!std::isfinite(x) || x == 0.0 || (float)x == 0.0f || std::isinf((float)x))
+      return fail(VLGQA_EINVAL, "q_scale", "scale products overflow or underflow f32");
+  if (batch == 0 || (seqlen_q == 0 && seqlen_k == 0)) return VLGQA_OK;
+  const int64_t rows = batch * seqlen_q, keys = batch * seqlen_k;
+  const vlgqa::BwdWorkspace w =
+      vlgqa::bwd_workspace(rows, keys, num_heads, num_kv_heads, head_dim, true);
+  if (workspace_floats < w.total)
+    return fail(VLGQA_EINVAL, "workspace_floats",
+                "smaller than vlgqa_bwd_workspace_floats(rows, keys, H, Hkv, D, 1)");
+  if ((rc = check_ptr(workspace, "workspace"))) return rc;
+  if (seqlen_k > 0) {
+    if ((rc = check_ptr(k, "k"))) return rc;
+    if ((rc = check_ptr(v, "v"))) return rc;
+    if ((rc = check_ptr(dk, "dk"))) return rc;
+    if ((rc = check_ptr(dv, "dv"))) return rc;
+  }
+  if (rows > 0) {  // the copies are checked again as q / dout below
+    if ((rc = check_ptr(dout, "dout"))) return rc;
+    if ((rc = check_ptr(q, "q"))) return rc;
+  }
+  vlgqa::BwdParams p{};
+  p.e4m3 = 1;
+  p.q8 = q; p.k8 = k; p.v8 = v; p.do8 = dout;
+  p.wq = workspace + w.wide;
+  p.wdo = workspace + w.wide + rows * num_heads * head_dim / 2;
+  p.wk = workspace + w.wide + rows * num_heads * head_dim;
+  p.wv = workspace + w.wide + rows * num_heads * head_dim + keys * num_kv_heads * head_dim / 2;
+  p.n_q = rows * num_heads * head_dim;
+  p.n_k = keys * num_kv_heads * head_dim;
+  p.dout = p.wdo; p.q = p.wq; p.k = p.wk; p.v = p.wv; p.o = out; p.lse = lse;
+  p.delta = workspace;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.cu_q = nullptr; p.cu_k = nullptr;
+  p.q_bs = num_heads * seqlen_q * head_dim; p.q_rs = head_dim; p.q_hs = seqlen_q * head_dim;
+  p.k_bs = num_kv_heads * seqlen_k * head_dim; p.k_rs = head_dim; p.k_hs = seqlen_k * head_dim;
+  p.l_bs = num_heads * seqlen_q; p.l_rs = 1; p.l_hs = seqlen_q;
+  p.batch = (int32_t)batch;
+  p.heads = (int32_t)num_heads;
+  p.kv_heads = (int32_t)num_kv_heads;
+  p.group = (int32_t)(num_heads / num_kv_heads);
+  p.seqlen_q = (int32_t)seqlen_q;
+  p.seqlen_k = (int32_t)seqlen_k;
+  p.causal = causal;
+  p.window = 0;
+  p.max_seqlen_q = (int32_t)seqlen_q;
+  p.max_seqlen_k = (int32_t)seqlen_k;
+  p.d_batch = (int32_t)batch; p.d_rows = (int32_t)seqlen_q;
+  p.kp_rows = (int32_t)keys;
+  p.part = workspace + w.part;
+  p.scale = (float)rs;
+  p.score_mul = (float)m[0];
+  p.dp_mul = (float)m[1];
+  p.dq_mul = (float)m[2];
+  p.dk_mul = (float)m[3];
+  p.dv_mul = (float)m[4];
+  p.delta_mul = (float)m[5];
+  return bwd_common(p, VLGQA_BF16, head_dim, rows, hip_stream);
 }
 
 static int check_pack_common(const int32_t* cu_seqlens, int64_t batch_size, int64_t max_seqlen,
