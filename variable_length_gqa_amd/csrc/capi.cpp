@@ -228,7 +228,7 @@ int flash_attention_decode(const void* q, const void* k, const void* v, int64_t 
   if (window_size < 0) return fail(VLGQA_EINVAL, "window_size", "must be non-negative");
   if (causal != 0 && causal != 1) return fail(VLGQA_EINVAL, "causal", "must be 0 or 1");
   const int64_t group = num_heads / num_kv_heads;
-  if (seqlen_q * group > 32)
+  if (seqlen_q > 32 || seqlen_q * group > 32)
     return fail(VLGQA_EINVAL, "seqlen_q",
                 "seqlen_q * num_heads / num_kv_heads must be at most 32 (use flash_attention_fwd)");
   const int64_t n = kv_seq_len < 0 ? kv_capacity : kv_seq_len;

@@ -76,10 +76,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void decode_kern
     for (int ks = 0; ks < C::NS; ++ks) qf[ks] = bload16(qr, (16 * ks + 8 * hl) * 2);
   }
 
-  // this wave's key tiles [t0, t1): contiguous slice of the visible range
-  int kv_lo = 0, kv_hi = n;
-  if (upper) kv_hi = min(n, p.seqlen_q - 1 + off + 1);
-  if (p.window > 0) kv_lo = max(0, off - p.window + 1);
+  // this wave's key tiles [t0, t1): a contiguous slice of the keys any row
+  // sees (the last query sits at key n - 1, so the causal bound is n itself)
+  const int kv_hi = n;
+  const int kv_lo = p.window > 0 ? max(0, off - p.window + 1) : 0;
   const int tiles_lo = kv_lo / 32, tiles_hi = kv_hi > kv_lo ? (kv_hi + 31) / 32 : tiles_lo;
   const int nt = tiles_hi - tiles_lo;
   const int t0 = tiles_lo + (int)((int64_t)nt * part / np);
