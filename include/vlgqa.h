@@ -33,6 +33,11 @@
  *     on the host before any HIP call is made.
  *   - Empty problems (no batch, no query rows, no heads' work) return VLGQA_OK
  *     without launching anything.
+ *   - Size limit: the kernels address one sequence's rows (of one head, in
+ *     the dense layouts) through 32-bit byte offsets, so (length + 128) x
+ *     (row stride in bytes) must stay below 4 GiB for q and for k/v (packed:
+ *     the row stride is heads x head_dim elements, e.g. 262,016 tokens at 64
+ *     bf16 heads of 128); longer sequences return EINVAL.
  */
 #ifndef VLGQA_H
 #define VLGQA_H

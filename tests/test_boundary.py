@@ -352,3 +352,20 @@ def test_bwd_workspace_sizes(lib):
     assert f(4, 5, 2, 1, 64, 1) == 16 + 4 * 5 * 64 + (4 * 2 + 5 * 1) * 64
     assert bwd8(lib, b=0, q=0, k=0, v=0, o=0, lse=0, dq=0, dk=0, dv=0, ws=0, wsf=0) == \
         _lib.VLGQA_OK
+
+
+def test_sequences_past_32bit_buffer_offsets_are_rejected(lib):
+    # one sequence's rows must span less than 4 GiB (the kernels' buffer
+    # descriptors use 32-bit byte offsets): 300000 tokens x 64 heads x 128 x 2 B
+    assert varlen(lib, h=64, hkv=8, d=128, dtype=BF16, mq=300000, mk=512, tq=300000,
+                  tk=300000) == EINVAL
+    assert err(lib).startswith("max_seqlen_q:"), err(lib)
+    assert varlen(lib, h=64, hkv=64, d=128, dtype=BF16, mq=512, mk=300000, tq=300000,
+                  tk=300000) == EINVAL
+    assert err(lib).startswith("max_seqlen_k:"), err(lib)
+    assert dense(lib, b=1, sq=1 << 24, cap=1 << 24, n=1 << 24) == EINVAL
+    assert err(lib).startswith("seqlen_q:"), err(lib)
+    assert decode(lib, b=1, cap=1 << 24, n=1 << 24) == EINVAL
+    assert err(lib).startswith("kv_seq_len:"), err(lib)
+    assert bwd8(lib, b=1, sq=64, sk=1 << 24) == EINVAL
+    assert err(lib).startswith("seqlen_k:"), err(lib)

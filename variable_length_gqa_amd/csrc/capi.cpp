@@ -47,6 +47,18 @@ int check_head_dim(int64_t head_dim) {
   return VLGQA_OK;
 }
 
+// The kernels address the rows of one sequence (and head) through a buffer
+// descriptor with 32-bit byte offsets, reading up to a tile past its end:
+// rows + 128 rows of row_bytes each must stay below 4 GiB.
+int check_span(int64_t rows, int64_t row_bytes, const char* name) {
+  if (rows > 0 && (rows + 128) * row_bytes > (int64_t)UINT32_MAX)
+    return fail(VLGQA_EINVAL, name,
+                "one sequence's rows span 4 GiB or more (32-bit buffer offsets)");
+  return VLGQA_OK;
+}
+
+int elem_bytes(int elem) { return elem == vlgqa::E_F32 ? 4 : elem == vlgqa::E_E4M3 ? 1 : 2; }
+
 int elem_of_dtype(int dtype, int* elem) {
   switch (dtype) {
     case VLGQA_F32: *elem = vlgqa::E_F32; return VLGQA_OK;
@@ -96,6 +108,11 @@ int varlen_attention_fwd(const void* q, const void* k, const void* v,
     return fail(VLGQA_EINVAL, "total_q", "token counts must fit I32 cu_seqlens");
   if (batch_size > INT32_MAX - 1) return fail(VLGQA_EINVAL, "batch_size", "too large");
   if (batch_size == 0 || total_q == 0 || max_seqlen_q == 0) return VLGQA_OK;
+  if ((rc = check_span(max_seqlen_q, num_heads * head_dim * elem_bytes(elem), "max_seqlen_q")))
+    return rc;
+  if ((rc = check_span(max_seqlen_k, num_kv_heads * head_dim * elem_bytes(elem),
+                       "max_seqlen_k")))
+    return rc;
   if ((rc = check_ptr(q, "q"))) return rc;
   if (total_k > 0) {
     if ((rc = check_ptr(k, "k"))) return rc;
@@ -143,6 +160,8 @@ static int dense_common(const void* q, const void* k, const void* v, int64_t bat
     return fail(VLGQA_EINVAL, "seqlen_q", "extents must fit 32 bits");
   if (window_size > INT32_MAX) window_size = INT32_MAX;
   if (batch == 0 || seqlen_q == 0) return VLGQA_OK;
+  if ((rc = check_span(seqlen_q, head_dim * elem_bytes(elem), "seqlen_q"))) return rc;
+  if ((rc = check_span(n, head_dim * elem_bytes(elem), "kv_seq_len"))) return rc;
   if ((rc = check_ptr(q, "q"))) return rc;
   if (n > 0) {
     if ((rc = check_ptr(k, "k"))) return rc;
@@ -237,6 +256,7 @@ int flash_attention_decode(const void* q, const void* k, const void* v, int64_t 
     return fail(VLGQA_EINVAL, "kv_capacity", "extents must fit 32 bits");
   if (window_size > INT32_MAX) window_size = INT32_MAX;
   if (batch == 0 || seqlen_q == 0) return VLGQA_OK;
+  if ((rc = check_span(n, head_dim * 2, "kv_seq_len"))) return rc;
   const int64_t need = vlgqa::decode_workspace_floats(batch, num_kv_heads, head_dim, n);
   const int64_t parts = vlgqa::decode_parts(batch, num_kv_heads, head_dim, n);
   if (batch * num_kv_heads * parts > INT32_MAX)
@@ -335,6 +355,8 @@ int varlen_attention_bwd(const void* dout, const void* q, const void* k, const v
   if (batch_size == 0 || (total_q == 0 && total_k == 0)) return VLGQA_OK;
   if (dtype == VLGQA_F32)
     return fail(VLGQA_EUNSUPPORTED, "dtype", "the backward is compiled for bf16 and f16 only");
+  if ((rc = check_span(max_seqlen_q, num_heads * head_dim * 2, "max_seqlen_q"))) return rc;
+  if ((rc = check_span(max_seqlen_k, num_kv_heads * head_dim * 2, "max_seqlen_k"))) return rc;
   if ((rc = check_ptr(cu_seqlens_q, "cu_seqlens_q"))) return rc;
   if ((rc = check_ptr(cu_seqlens_k, "cu_seqlens_k"))) return rc;
   if (total_k > 0) {
@@ -388,6 +410,8 @@ int flash_attention_bwd(const void* dout, const void* q, const void* k, const vo
   if (batch == 0 || (seqlen_q == 0 && seqlen_k == 0)) return VLGQA_OK;
   if (dtype == VLGQA_F32)
     return fail(VLGQA_EUNSUPPORTED, "dtype", "the backward is compiled for bf16 and f16 only");
+  if ((rc = check_span(seqlen_q, head_dim * 2, "seqlen_q"))) return rc;
+  if ((rc = check_span(seqlen_k, head_dim * 2, "seqlen_k"))) return rc;
   if (seqlen_k > 0) {
     if ((rc = check_ptr(k, "k"))) return rc;
     if ((rc = check_ptr(v, "v"))) return rc;
@@ -464,6 +488,8 @@ int flash_attention_bwd_fp8(const void* dout, const void* q, const void* k, cons
     if (!std::isfinite(x) || x == 0.0 || (float)x == 0.0f || std::isinf((float)x))
       return fail(VLGQA_EINVAL, "q_scale", "scale products overflow or underflow f32");
   if (batch == 0 || (seqlen_q == 0 && seqlen_k == 0)) return VLGQA_OK;
+  if ((rc = check_span(seqlen_q, head_dim * 2, "seqlen_q"))) return rc;
+  if ((rc = check_span(seqlen_k, head_dim * 2, "seqlen_k"))) return rc;
   const int64_t rows = batch * seqlen_q, keys = batch * seqlen_k;
   const vlgqa::BwdWorkspace w =
       vlgqa::bwd_workspace(rows, keys, num_heads, num_kv_heads, head_dim, true);
