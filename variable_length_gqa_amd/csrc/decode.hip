@@ -7,8 +7,8 @@
 //     queries (row r = (head r / S_q, query r % S_q)), padded to the 32 rows of
 //     one MFMA tile: K and V are read once for the whole GQA group;
 //   * the keys are split into NP contiguous slices, one wave each (a workgroup
-//     is one wave): each wave streams its slice through a private, double
-//     buffered LDS region by DMA (32-key tiles, no barriers) and keeps the
+//     is one wave): each wave streams its slice through a private LDS ring of
+//     three K/V tile pairs by DMA (32-key tiles, no barriers) and keeps the
 //     online-softmax state of the forward kernel (S^T = K Q^T and
 //     O^T += V^T P^T on v_mfma_f32_32x32x16, optimistic reference maximum);
 //   * each wave writes its partial (unnormalised O, reference maximum m,
