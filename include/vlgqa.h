@@ -261,14 +261,14 @@ int flash_attention_bwd(const void* dout, const void* q, const void* k, const vo
  *
  * The gradients are those of flash_attention_bwd on the dequantised inputs
  * (scale 1/sqrt(head_dim); causal or no mask: this method takes no window),
- * with delta_i = dout_i . out_i taken from the stored output.  f32
- * accumulation; P and dS are rounded to bf16 before the products that use
- * them.
+ * with delta_i = dout_i . out_i taken from the stored output.  S = q k^T and
+ * dP = dout v^T run on the FP8 matrix cores from the codes; P and dS are
+ * rounded to bf16 for the dv, dk and dq products; f32 accumulation.
  *
  * workspace: float32, 16-byte aligned, workspace_floats >=
  * vlgqa_bwd_workspace_floats(batch * seqlen_q, batch * seqlen_k, num_heads,
  * num_kv_heads, head_dim, 1): the 16-bit layout followed by bf16 copies of the
- * codes of q, dout, k and v.  Contents on return are unspecified.
+ * codes of q, dout and k.  Contents on return are unspecified.
  *
  * Errors: EINVAL for a scale that is not finite and positive, scale products
  * outside the f32 range, a workspace that is too small, and as

@@ -348,8 +348,8 @@ def test_bwd_workspace_sizes(lib):
     # row planes rounded up to 16 bytes, then 4 D floats per key and kv head
     assert f(3, 5, 1, 1, 64, 0) == 8 + 4 * 5 * 64
     assert f(4, 5, 2, 1, 64, 0) == 16 + 4 * 5 * 64
-    # E4M3: plus bf16 copies of q and dout (rows x heads) and k and v (keys x kv heads)
-    assert f(4, 5, 2, 1, 64, 1) == 16 + 4 * 5 * 64 + (4 * 2 + 5 * 1) * 64
+    # E4M3: plus bf16 copies of q and dout (rows x heads) and of k (keys x kv heads)
+    assert f(4, 5, 2, 1, 64, 1) == 16 + 4 * 5 * 64 + 4 * 2 * 64 + 5 * 1 * 64 // 2
     assert bwd8(lib, b=0, q=0, k=0, v=0, o=0, lse=0, dq=0, dk=0, dv=0, ws=0, wsf=0) == \
         _lib.VLGQA_OK
 

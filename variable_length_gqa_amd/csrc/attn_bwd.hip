@@ -75,14 +75,6 @@ __device__ __forceinline__ float hi16(uint32_t w) {
   }
 }
 
-// two E4M3 codes (bytes 0-1 or 2-3 of w) -> two bf16 values, exact
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
-                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
 // Workspace layout (f32): [2][B][H][rows]: plane 0 = LSE * log2(e) (+inf for a
 // row with no visible key, so its weights are exp2(-inf) = 0), plane 1 = delta.
 // Dense: rows = S_q per batch; packed: B = 1 and rows = total_q.
@@ -158,7 +150,7 @@ __global__ __launch_bounds__(256) void bwd_rowsum8_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {
-        const uint32_t x = e4m3x2_to_bf16x2(a[i], hi), y = e4m3x2_to_bf16x2(c[i], hi);
+        const uint32_t x = fp8x2_to_bf16x2(a[i], hi), y = fp8x2_to_bf16x2(c[i], hi);
         acc += lo16<E_BF16>(x) * lo16<E_BF16>(y) + hi16<E_BF16>(x) * hi16<E_BF16>(y);
       }
   }
@@ -178,10 +170,10 @@ __global__ __launch_bounds__(256) void widen_e4m3_kernel(const uint8_t* __restri
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n16) return;
   const u32x4 c = *reinterpret_cast<const u32x4*>(src + i * 16);
-  const u32x4 lo = {e4m3x2_to_bf16x2(c[0], false), e4m3x2_to_bf16x2(c[0], true),
-                    e4m3x2_to_bf16x2(c[1], false), e4m3x2_to_bf16x2(c[1], true)};
-  const u32x4 hi = {e4m3x2_to_bf16x2(c[2], false), e4m3x2_to_bf16x2(c[2], true),
-                    e4m3x2_to_bf16x2(c[3], false), e4m3x2_to_bf16x2(c[3], true)};
+  const u32x4 lo = {fp8x2_to_bf16x2(c[0], false), fp8x2_to_bf16x2(c[0], true),
+                    fp8x2_to_bf16x2(c[1], false), fp8x2_to_bf16x2(c[1], true)};
+  const u32x4 hi = {fp8x2_to_bf16x2(c[2], false), fp8x2_to_bf16x2(c[2], true),
+                    fp8x2_to_bf16x2(c[3], false), fp8x2_to_bf16x2(c[3], true)};
   *reinterpret_cast<u32x4*>(dst + i * 16) = lo;
   *reinterpret_cast<u32x4*>(dst + i * 16 + 8) = hi;
 }
@@ -249,6 +241,26 @@ __device__ __forceinline__ uint32_t row_read_off(int ql, int hl) {
   return (uint32_t)ql * T16<D>::ROWB + (uint32_t)((hl ^ swz<D>(ql)) * 16);
 }
 
+// E4M3 tiles (32 rows of D codes, 16-byte chunks XOR-swizzled by swz8): the
+// DMA chunk of thread tid (row tid / (D/16)); false for threads past the
+// tile's 2 D chunks (D = 64: waves 2 and 3)
+template <int D>
+__device__ __forceinline__ bool tile8_dma_offset(uint32_t& voff, int tid, uint32_t rs) {
+  const int crow = tid / (D / 16), cch = tid % (D / 16);
+  voff = (uint32_t)crow * rs + (uint32_t)((cch ^ swz8<D>(crow)) * 16);
+  return tid < 2 * D;
+}
+
+// the A (or B) operand of v_mfma_f32_32x32x64_f8f6f4 for k-step ks: row ql,
+// codes 64 ks + 32 hl .. +32, as two 16-byte LDS reads
+template <int D>
+__device__ __forceinline__ void tile8_read(const uint8_t* t, int ql, int hl, int ks, u32x4 (&a)[2]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    a[c] = *reinterpret_cast<const u32x4*>(
+        t + (uint32_t)ql * D + (uint32_t)(((4 * ks + 2 * hl + c) ^ swz8<D>(ql)) * 16));
+}
+
 // transposing-read offsets (the forward's V^T operand)
 template <int D>
 __device__ __forceinline__ void tr_read_offsets(uint32_t (&o)[T16<D>::NOB][2], int lane) {
@@ -308,13 +320,23 @@ __device__ __forceinline__ void store_rows_e4m3(void* base, int64_t row_off, int
 // which costs less than running one fused kernel at one wave per SIMD.
 enum : int { MODE_DV = 0, MODE_DK = 1 };
 
-template <int ELEM, int D, int MODE>
+// E8: E4M3 inputs.  S = Q K^T (and dP = dO V^T) run on the FP8 matrix cores
+// from the codes (K^T / V^T codes in registers, Q / dO code tiles in LDS); the
+// accumulation products keep the bf16 copies (dO tile for dV, Q tile for dK).
+template <int ELEM, int D, int MODE, int E8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(MODE == MODE_DV ? 3 : 2, MODE == MODE_DV ? 3 : 2)))
 void bwd_kv_kernel(BwdParams p) {
   using C = T16<D>;
-  // stage buffer: Q tile, dO tile, then 32 lse2 + 32 delta floats
-  constexpr int STAGE = 2 * C::TILE + 256;
+  constexpr int T8 = 32 * D;  // bytes of an E4M3 tile
+  // stage buffer (byte offsets): the S operand tile, the dP operand tile (dK),
+  // the transposed-read tile of the accumulation, then 32 lse2 + 32 delta
+  // floats.  16-bit: Q, dO (both roles); E8 dV: Q8, dO; E8 dK: Q8, dO8, Q.
+  constexpr int OFF_S = 0;
+  constexpr int OFF_DP = E8 ? T8 : C::TILE;
+  constexpr int OFF_T = !E8 ? (MODE == MODE_DV ? C::TILE : 0) : (MODE == MODE_DV ? T8 : 2 * T8);
+  constexpr int OFF_W = !E8 ? 2 * C::TILE : (MODE == MODE_DV ? T8 + C::TILE : 2 * T8 + C::TILE);
+  constexpr int STAGE = OFF_W + 256;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
   // work: a "stream" is (batch, kv head, split) -- the query heads whose Q /
@@ -346,19 +368,28 @@ void bwd_kv_kernel(BwdParams p) {
   const float mul = p.score_mul;
   const float dpm = p.dp_mul;
 
-  // K^T (and for dK V^T) fragments of the lane's key: k[key][16 ks + 8 hl .. +8]
-  u32x4 kf[C::NS], vf[MODE == MODE_DK ? C::NS : 1];
+  // K^T (and for dK V^T) B operands of the lane's key: 16-bit k[key][16 ks +
+  // 8 hl .. +8]; E8 codes k8[key][64 ks + 32 hl .. +32]
+  constexpr int NSB = E8 ? D / 64 : C::NS;
+  u32x4 kf[NSB][E8 ? 2 : 1], vf[MODE == MODE_DK ? NSB : 1][E8 ? 2 : 1];
   {
+    const int eb = E8 ? 1 : 2;
     const int64_t koff = ((int64_t)b * p.k_bs + (int64_t)sb.k_start * p.k_rs +
-                          (int64_t)kvh * p.k_hs) * 2;
-    const uint32_t bytes = sat_bytes((int64_t)sb.Lk * p.k_rs * 2);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
-    const uint32_t roff = (uint32_t)key * (uint32_t)(p.k_rs * 2);
+                          (int64_t)kvh * p.k_hs) * eb;
+    const uint32_t bytes = sat_bytes((int64_t)sb.Lk * p.k_rs * eb);
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(E8 ? p.k8 : p.k);
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(E8 ? p.v8 : p.v);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + koff, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + koff, bytes);
+    const uint32_t roff = (uint32_t)key * (uint32_t)(p.k_rs * eb);
 #pragma unroll
-    for (int ks = 0; ks < C::NS; ++ks) {
-      kf[ks] = bload16(kr, roff + (16 * ks + 8 * hl) * 2);
-      if constexpr (MODE == MODE_DK) vf[ks] = bload16(vr, roff + (16 * ks + 8 * hl) * 2);
+    for (int ks = 0; ks < NSB; ++ks) {
+#pragma unroll
+      for (int c = 0; c < (E8 ? 2 : 1); ++c) {
+        const uint32_t o = E8 ? roff + 64 * ks + 32 * hl + 16 * c : roff + (16 * ks + 8 * hl) * 2;
+        kf[ks][c] = bload16(kr, o);
+        if constexpr (MODE == MODE_DK) vf[ks][c] = bload16(vr, o);
+      }
     }
   }
   f32x16 acc[C::NOB];
@@ -382,30 +413,45 @@ void bwd_kv_kernel(BwdParams p) {
 
   uint32_t voff[C::CPT];
   tile_dma_offsets<D>(voff, wid, lane, (uint32_t)(p.q_rs * 2));
+  uint32_t voff8 = 0;
+  const bool has8 = E8 ? tile8_dma_offset<D>(voff8, tid, (uint32_t)p.q_rs) : false;
   const uint32_t roff0 = row_read_off<D>(ql, hl);
   uint32_t troff[C::NOB][2];
   tr_read_offsets<D>(troff, lane);
   const int64_t plane = ws_plane(p);
 
-  // DMA of stage s into buffer u: Q and dO tiles of (head, tile), lse2/delta
+  // DMA of stage s into buffer u: the tiles of (head, tile) and its lse2/delta
   auto issue = [&](int s, int u) __attribute__((always_inline)) {
     const int hh = s / nt, t = tb - 1 - s % nt;
     const int h = hbase + hh;
-    const int64_t qoff = ((int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs +
-                          (int64_t)h * p.q_hs) * 2;
+    const int64_t qrow0 = (int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs + (int64_t)h * p.q_hs;
     const uint32_t bytes = sat_bytes((int64_t)sb.Lq * p.q_rs * 2);
     const uint32_t base = (uint32_t)(t * 32) * (uint32_t)(p.q_rs * 2);
     const uint8_t* buf = lds + u * STAGE;
-    dma_tile16<D>(buf, rsrc_words(reinterpret_cast<const uint8_t*>(p.q) + qoff, bytes), base,
-                  wid, voff);
-    dma_tile16<D>(buf + C::TILE, rsrc_words(reinterpret_cast<const uint8_t*>(p.dout) + qoff, bytes),
-                  base, wid, voff);
+    const u32x4 q16 = rsrc_words(reinterpret_cast<const uint8_t*>(p.q) + qrow0 * 2, bytes);
+    const u32x4 d16 = rsrc_words(reinterpret_cast<const uint8_t*>(p.dout) + qrow0 * 2, bytes);
+    if constexpr (!E8) {
+      dma_tile16<D>(buf, q16, base, wid, voff);
+      dma_tile16<D>(buf + C::TILE, d16, base, wid, voff);
+    } else {
+      const uint32_t bytes8 = sat_bytes((int64_t)sb.Lq * p.q_rs);
+      const uint32_t base8 = (uint32_t)(t * 32) * (uint32_t)p.q_rs;
+      const uint32_t l8 = (uint32_t)(uintptr_t)(lds_void*)buf + wid * 1024;
+      if (has8) {
+        dma16(l8 + OFF_S, base8 + voff8,
+              rsrc_words(reinterpret_cast<const uint8_t*>(p.q8) + qrow0, bytes8));
+        if constexpr (MODE == MODE_DK)
+          dma16(l8 + OFF_DP, base8 + voff8,
+                rsrc_words(reinterpret_cast<const uint8_t*>(p.do8) + qrow0, bytes8));
+      }
+      dma_tile16<D>(buf + OFF_T, MODE == MODE_DV ? d16 : q16, base, wid, voff);
+    }
     if (wid < 2 && lane < 8) {
       // wave 0: lse2 of rows 32 t .. +32 (4 per lane), wave 1: delta; rows past
       // the sequence arrive as zeros
       const int64_t wi = ws_index(p, p.cu_q ? 0 : b, p.cu_q ? (int64_t)sb.q_start : 0, h);
       const float* src = p.delta + wi + (wid == 1 ? plane : 0);
-      dma16((uint32_t)(uintptr_t)(lds_void*)(buf + 2 * C::TILE + wid * 128),
+      dma16((uint32_t)(uintptr_t)(lds_void*)(buf + OFF_W + wid * 128),
             (uint32_t)(t * 32 * 4 + lane * 16), rsrc_words(src, sat_bytes((int64_t)sb.Lq * 4)));
     }
   };
@@ -420,16 +466,30 @@ void bwd_kv_kernel(BwdParams p) {
     const int t = tb - 1 - s % nt;
     const int q0 = t * 32;
     if (wave_keys && q0 < wqb && q0 + 32 > wqa) {
-      const uint8_t* qt = lds + u * STAGE;
-      const uint8_t* dot = qt + C::TILE;
-      const float* wsv = reinterpret_cast<const float*>(qt + 2 * C::TILE);
+      const uint8_t* sbuf = lds + u * STAGE;
+      const uint8_t* st_ = sbuf + OFF_S;    // A operand of S (Q rows)
+      const uint8_t* dpt = sbuf + OFF_DP;   // A operand of dP (dO rows)
+      const float* wsv = reinterpret_cast<const float*>(sbuf + OFF_W);
       f32x16 sc = {}, dp = {};
+      if constexpr (!E8) {
 #pragma unroll
-      for (int ks = 0; ks < C::NS; ++ks) {
-        const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
-        sc = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(qt + ro), kf[ks], sc);
-        if constexpr (MODE == MODE_DK)
-          dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(dot + ro), vf[ks], dp);
+        for (int ks = 0; ks < C::NS; ++ks) {
+          const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
+          sc = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(st_ + ro), kf[ks][0], sc);
+          if constexpr (MODE == MODE_DK)
+            dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(dpt + ro), vf[ks][0], dp);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < NSB; ++ks) {
+          u32x4 a[2];
+          tile8_read<D>(st_, ql, hl, ks, a);
+          sc = mfma_fp8(a, kf[ks], sc);
+          if constexpr (MODE == MODE_DK) {
+            tile8_read<D>(dpt, ql, hl, ks, a);
+            dp = mfma_fp8(a, vf[ks], dp);
+          }
+        }
       }
       // register r holds query row q0 + qq(r) + 4 hl, qq(r) = 8 (r / 4) + r % 4
       f32x4 l2[4], dl[4];
@@ -474,7 +534,7 @@ void bwd_kv_kernel(BwdParams p) {
         }
       }
       // dV^T += dO^T P  or  dK^T += Q^T dS  (A by transposing reads)
-      const uint8_t* at = MODE == MODE_DV ? dot : qt;
+      const uint8_t* at = sbuf + OFF_T;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
@@ -573,10 +633,14 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
 // dQ
 // ---------------------------------------------------------------------------
 
-template <int ELEM, int D>
+// E8: E4M3 inputs.  S^T = K Q^T and dP^T = V dO^T run on the FP8 matrix cores
+// (Q^T / dO^T codes in registers, K / V code tiles in LDS, in the second half
+// of the lv buffers); dQ^T += K^T dS^T keeps the bf16 copy of the K tile.
+template <int ELEM, int D, int E8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
   using C = T16<D>;
+  constexpr int T8 = 32 * D;  // bytes of an E4M3 tile
   __shared__ __attribute__((aligned(1024))) uint8_t lk0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lk1[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lv0[C::TILE];
@@ -606,19 +670,28 @@ void bwd_dq_kernel(BwdParams p) {
   const int off = sb.Lk - sb.Lq;
   const bool upper = p.causal || p.window > 0;
 
-  // Q^T and dO^T fragments of the lane's row, and its lse2 / delta
-  u32x4 qf[C::NS], of[C::NS];
+  // Q^T and dO^T B operands of the lane's row (16-bit: [16 ks + 8 hl .. +8];
+  // E8 codes: [64 ks + 32 hl .. +32]), and its lse2 / delta
+  constexpr int NSB = E8 ? D / 64 : C::NS;
+  u32x4 qf[NSB][E8 ? 2 : 1], of[NSB][E8 ? 2 : 1];
   {
+    const int eb = E8 ? 1 : 2;
     const int64_t qoff = ((int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs +
-                          (int64_t)h * p.q_hs) * 2;
-    const uint32_t bytes = sat_bytes((int64_t)sb.Lq * p.q_rs * 2);
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(reinterpret_cast<const uint8_t*>(p.q) + qoff, bytes);
-    const __amdgpu_buffer_rsrc_t dr = make_rsrc(reinterpret_cast<const uint8_t*>(p.dout) + qoff, bytes);
-    const uint32_t roff = (uint32_t)qrow * (uint32_t)(p.q_rs * 2);
+                          (int64_t)h * p.q_hs) * eb;
+    const uint32_t bytes = sat_bytes((int64_t)sb.Lq * p.q_rs * eb);
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(E8 ? p.q8 : p.q);
+    const uint8_t* dbase = reinterpret_cast<const uint8_t*>(E8 ? p.do8 : p.dout);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qbase + qoff, bytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dbase + qoff, bytes);
+    const uint32_t roff = (uint32_t)qrow * (uint32_t)(p.q_rs * eb);
 #pragma unroll
-    for (int ks = 0; ks < C::NS; ++ks) {
-      qf[ks] = bload16(qr, roff + (16 * ks + 8 * hl) * 2);
-      of[ks] = bload16(dr, roff + (16 * ks + 8 * hl) * 2);
+    for (int ks = 0; ks < NSB; ++ks) {
+#pragma unroll
+      for (int c = 0; c < (E8 ? 2 : 1); ++c) {
+        const uint32_t o = E8 ? roff + 64 * ks + 32 * hl + 16 * c : roff + (16 * ks + 8 * hl) * 2;
+        qf[ks][c] = bload16(qr, o);
+        of[ks][c] = bload16(dr, o);
+      }
     }
   }
   float lse2 = INFINITY, dlt = 0.0f;
@@ -628,18 +701,39 @@ void bwd_dq_kernel(BwdParams p) {
     dlt = p.delta[ws_plane(p) + wi];
   }
 
-  u32x4 krs, vrs;
+  // descriptors: 16-bit K and V tiles; E8: the bf16 K copy and the K / V codes
+  u32x4 krs, vrs = {}, k8rs = {}, v8rs = {};
   uint32_t rs;
   {
-    const int64_t koff = ((int64_t)b * p.k_bs + (int64_t)sb.k_start * p.k_rs +
-                          (int64_t)kvh * p.k_hs) * 2;
+    const int64_t krow0 = (int64_t)b * p.k_bs + (int64_t)sb.k_start * p.k_rs +
+                          (int64_t)kvh * p.k_hs;
     const uint32_t bytes = sat_bytes((int64_t)sb.Lk * p.k_rs * 2);
-    krs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
-    vrs = rsrc_words(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
+    krs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k) + krow0 * 2, bytes);
+    if constexpr (!E8) vrs = rsrc_words(reinterpret_cast<const uint8_t*>(p.v) + krow0 * 2, bytes);
     rs = (uint32_t)(p.k_rs * 2);
+    if constexpr (E8) {
+      const uint32_t bytes8 = sat_bytes((int64_t)sb.Lk * p.k_rs);
+      k8rs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k8) + krow0, bytes8);
+      v8rs = rsrc_words(reinterpret_cast<const uint8_t*>(p.v8) + krow0, bytes8);
+    }
   }
   uint32_t voff[C::CPT];
   tile_dma_offsets<D>(voff, wid, lane, rs);
+  uint32_t voff8 = 0;
+  const bool has8 = E8 ? tile8_dma_offset<D>(voff8, tid, (uint32_t)p.k_rs) : false;
+  // one key tile into (kbuf, vbuf): 16-bit K and V; E8: bf16 K, K codes and
+  // V codes (the two code tiles in vbuf)
+  auto dma_kv = [&](const uint8_t* kbuf, const uint8_t* vbuf, int t) __attribute__((always_inline)) {
+    dma_tile16<D>(kbuf, krs, (uint32_t)(t * 32) * rs, wid, voff);
+    if constexpr (!E8) {
+      dma_tile16<D>(vbuf, vrs, (uint32_t)(t * 32) * rs, wid, voff);
+    } else if (has8) {
+      const uint32_t base8 = (uint32_t)(t * 32) * (uint32_t)p.k_rs;
+      const uint32_t l8 = (uint32_t)(uintptr_t)(lds_void*)vbuf + wid * 1024;
+      dma16(l8, base8 + voff8, k8rs);
+      dma16(l8 + T8, base8 + voff8, v8rs);
+    }
+  };
   const uint32_t roff0 = row_read_off<D>(ql, hl);
   uint32_t troff[C::NOB][2];
   tr_read_offsets<D>(troff, lane);
@@ -661,28 +755,32 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < C::NOB; ++i) dq[i] = f32x16{};
 
-  if (t0 < t1) {
-    dma_tile16<D>(lk0, krs, (uint32_t)(t0 * 32) * rs, wid, voff);
-    dma_tile16<D>(lv0, vrs, (uint32_t)(t0 * 32) * rs, wid, voff);
-  }
+  if (t0 < t1) dma_kv(lk0, lv0, t0);
   wait_vm_all();
   lds_barrier();
 
   auto tile = [&](int t, const uint8_t* kb_, const uint8_t* vb_, const uint8_t* knext,
                   const uint8_t* vnext) __attribute__((always_inline)) {
-    if (t + 1 < t1) {
-      const uint32_t base = (uint32_t)((t + 1) * 32) * rs;
-      dma_tile16<D>(knext, krs, base, wid, voff);
-      dma_tile16<D>(vnext, vrs, base, wid, voff);
-    }
+    if (t + 1 < t1) dma_kv(knext, vnext, t + 1);
     const int c0 = t * 32;
     if (wa <= wb && c0 < whi && c0 + 32 > wlo) {
       f32x16 sc = {}, dp = {};
+      if constexpr (!E8) {
 #pragma unroll
-      for (int ks = 0; ks < C::NS; ++ks) {
-        const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
-        sc = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(kb_ + ro), qf[ks], sc);
-        dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(vb_ + ro), of[ks], dp);
+        for (int ks = 0; ks < C::NS; ++ks) {
+          const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
+          sc = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(kb_ + ro), qf[ks][0], sc);
+          dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(vb_ + ro), of[ks][0], dp);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < NSB; ++ks) {
+          u32x4 a[2];
+          tile8_read<D>(vb_, ql, hl, ks, a);
+          sc = mfma_fp8(a, qf[ks], sc);
+          tile8_read<D>(vb_ + T8, ql, hl, ks, a);
+          dp = mfma_fp8(a, of[ks], dp);
+        }
       }
       // register r holds key c0 + kk(r) + 4 hl, kk(r) = 8 (r / 4) + r % 4
       const bool need_mask = (c0 + 32 > sb.Lk) || (upper && c0 + 31 > wa + off) ||
@@ -764,7 +862,8 @@ BwdWorkspace bwd_workspace(int64_t rows, int64_t keys, int64_t heads, int64_t kv
   BwdWorkspace w;
   w.part = (2 * rows * heads + 3) / 4 * 4;  // 16-byte aligned parts
   w.wide = w.part + 4 * keys * kv_heads * head_dim;
-  w.total = w.wide + (e4m3 ? (rows * heads + keys * kv_heads) * head_dim : 0);
+  // E4M3: bf16 copies of q and dout (rows x heads), and of k (keys x kv heads)
+  w.total = w.wide + (e4m3 ? rows * heads * head_dim + keys * kv_heads * head_dim / 2 : 0);
   return w;
 }
 
@@ -779,8 +878,9 @@ hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t st
   const bool reduce = p.n_split > 1 || p.e4m3;
   if (p.e4m3) {
     // bf16 copies of the codes, then the row terms from the codes of dO and O
-    const struct { const void* src; void* dst; int64_t n; } w[4] = {
-        {p.q8, p.wq, p.n_q}, {p.do8, p.wdo, p.n_q}, {p.k8, p.wk, p.n_k}, {p.v8, p.wv, p.n_k}};
+    // (V is only an operand of dP, which runs on the codes)
+    const struct { const void* src; void* dst; int64_t n; } w[3] = {
+        {p.q8, p.wq, p.n_q}, {p.do8, p.wdo, p.n_q}, {p.k8, p.wk, p.n_k}};
     for (const auto& t : w)
       if (t.n > 0)
         hipLaunchKernelGGL(widen_e4m3_kernel, dim3((unsigned)((t.n / 16 + 255) / 256)), dim3(256),
@@ -791,20 +891,22 @@ hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t st
       else hipLaunchKernelGGL((bwd_rowsum8_kernel<64>), g0, blk, 0, stream, p);
     }
   }
-#define VLGQA_BWD(E, D)                                                        \
+#define VLGQA_BWD(E, D, E8)                                                    \
   do {                                                                         \
-    if (pairs > 0 && !p.e4m3)                                                  \
+    if (pairs > 0 && !E8)                                                      \
       hipLaunchKernelGGL((bwd_rowsum_kernel<E, D>), g0, blk, 0, stream, p);    \
-    if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DV>), g1, blk, 0, stream, p); \
-    if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DK>), g1, blk, 0, stream, p); \
-    if (g2.x > 0) hipLaunchKernelGGL((bwd_dq_kernel<E, D>), g2, blk, 0, stream, p);     \
+    if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DV, E8>), g1, blk, 0, stream, p); \
+    if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DK, E8>), g1, blk, 0, stream, p); \
+    if (g2.x > 0) hipLaunchKernelGGL((bwd_dq_kernel<E, D, E8>), g2, blk, 0, stream, p);     \
     if (reduce && g3.x > 0)                                                              \
       hipLaunchKernelGGL((bwd_reduce_kernel<E, D>), g3, blk, 0, stream, p);              \
   } while (0)
-  if (head_dim == 128 && elem == E_BF16) VLGQA_BWD(E_BF16, 128);
-  else if (head_dim == 128 && elem == E_F16) VLGQA_BWD(E_F16, 128);
-  else if (head_dim == 64 && elem == E_BF16) VLGQA_BWD(E_BF16, 64);
-  else if (head_dim == 64 && elem == E_F16) VLGQA_BWD(E_F16, 64);
+  if (p.e4m3 && head_dim == 128) VLGQA_BWD(E_BF16, 128, 1);
+  else if (p.e4m3 && head_dim == 64) VLGQA_BWD(E_BF16, 64, 1);
+  else if (head_dim == 128 && elem == E_BF16) VLGQA_BWD(E_BF16, 128, 0);
+  else if (head_dim == 128 && elem == E_F16) VLGQA_BWD(E_F16, 128, 0);
+  else if (head_dim == 64 && elem == E_BF16) VLGQA_BWD(E_BF16, 64, 0);
+  else if (head_dim == 64 && elem == E_F16) VLGQA_BWD(E_F16, 64, 0);
   else return hipErrorInvalidValue;
 #undef VLGQA_BWD
   return hipGetLastError();

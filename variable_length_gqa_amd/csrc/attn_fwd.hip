@@ -495,35 +495,6 @@ struct Cfg8 {
   static_assert(NCH <= kThreads && NCH % 64 == 0, "tile shape");
 };
 
-// chunk swizzle of an E4M3 K row in LDS: the 16 lanes of a K read cover 16
-// consecutive rows of one logical chunk; the swizzle is a bijection on the
-// rows of equal parity (D=128, 8 chunks a row) or equal residue mod 4 (D=64,
-// 4 chunks), so the 16 reads fall in distinct banks.
-template <int D>
-__device__ __forceinline__ int swz8(int row) {
-  if constexpr (D == 128) return (row >> 1) & 7;
-  else return (row >> 2) & 3;
-}
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x16 mfma_fp8(const u32x4 (&a)[2], const u32x4 (&b)[2], f32x16 c) {
-  const i32x8 av = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3],
-                    (int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
-  const i32x8 bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
-                    (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
-  // format selectors 0/0: both operands OCP E4M3; zero block scales = no scaling
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
-}
-
-// two E4M3 codes (bytes 0-1 or 2-3 of w) -> two bf16 in one register, exact
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
-  const bf16x2_t r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
-                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void fwd8_kernel(FwdParams p) {

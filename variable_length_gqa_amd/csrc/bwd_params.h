@@ -45,10 +45,12 @@ struct BwdParams {
   // multipliers of dP = dO.V^T and of the stored dq, dk, dv (16-bit inputs:
   // 1, 1/sqrt(D), 1/sqrt(D), 1; E4M3 inputs: the per-tensor scales folded in)
   float dp_mul, dq_mul, dk_mul, dv_mul;
-  // E4M3 path: q, k, v, dout point at bf16 copies of the codes (exact,
-  // unscaled) made by the widening kernel from q8 .. do8; delta is taken from
-  // the codes of dout and o times delta_mul; dq, dk, dv are E4M3 codes (dk, dv
-  // always through the f32 partials)
+  // E4M3 path: q8, k8, v8, do8 are the codes, the operands of the products
+  // S = Q K^T and dP = dO V^T on the FP8 matrix cores; q, k and dout point at
+  // bf16 copies of the codes (exact, unscaled, made by the widening kernel)
+  // for the transposed operands of the dK, dQ and dV accumulations; delta is
+  // taken from the codes of dout and o times delta_mul; dq, dk, dv are E4M3
+  // codes (dk, dv always through the f32 partials)
   int32_t e4m3;
   float delta_mul;
   const void* q8;
@@ -58,13 +60,12 @@ struct BwdParams {
   // bf16 copies (in the workspace) and their element counts
   void* wq;
   void* wk;
-  void* wv;
   void* wdo;
-  int64_t n_q, n_k;   // elements of q (= dout) and of k (= v)
+  int64_t n_q, n_k;   // elements of q (= dout) and of k
 };
 
 // float32 workspace of the backward: the row planes (LSE log2 e, delta), the
-// dk / dv partials, and for E4M3 inputs the bf16 copies of q, dout, k and v;
+// dk / dv partials, and for E4M3 inputs the bf16 copies of q, dout and k;
 // returns the offsets of the parts in floats
 struct BwdWorkspace {
   int64_t part, wide, total;

@@ -513,10 +513,9 @@ int flash_attention_bwd_fp8(const void* dout, const void* q, const void* k, cons
   p.wq = workspace + w.wide;
   p.wdo = workspace + w.wide + rows * num_heads * head_dim / 2;
   p.wk = workspace + w.wide + rows * num_heads * head_dim;
-  p.wv = workspace + w.wide + rows * num_heads * head_dim + keys * num_kv_heads * head_dim / 2;
   p.n_q = rows * num_heads * head_dim;
   p.n_k = keys * num_kv_heads * head_dim;
-  p.dout = p.wdo; p.q = p.wq; p.k = p.wk; p.v = p.wv; p.o = out; p.lse = lse;
+  p.dout = p.wdo; p.q = p.wq; p.k = p.wk; p.v = nullptr; p.o = out; p.lse = lse;
   p.delta = workspace;
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.cu_q = nullptr; p.cu_k = nullptr;
