@@ -325,7 +325,8 @@ enum : int { MODE_DV = 0, MODE_DK = 1 };
 // accumulation products keep the bf16 copies (dO tile for dV, Q tile for dK).
 template <int ELEM, int D, int MODE, int E8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(MODE == MODE_DV ? 3 : 2, MODE == MODE_DV ? 3 : 2)))
+                          amdgpu_waves_per_eu(MODE == MODE_DV || E8 || D == 64 ? 3 : 2,
+                                              MODE == MODE_DV || E8 || D == 64 ? 3 : 2)))
 void bwd_kv_kernel(BwdParams p) {
   using C = T16<D>;
   constexpr int T8 = 32 * D;  // bytes of an E4M3 tile
@@ -492,13 +493,7 @@ void bwd_kv_kernel(BwdParams p) {
         }
       }
       // register r holds query row q0 + qq(r) + 4 hl, qq(r) = 8 (r / 4) + r % 4
-      f32x4 l2[4], dl[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        l2[j] = *reinterpret_cast<const f32x4*>(wsv + 8 * j + 4 * hl);
-        if constexpr (MODE == MODE_DK)
-          dl[j] = *reinterpret_cast<const f32x4*>(wsv + 32 + 8 * j + 4 * hl);
-      }
+
       const bool need_mask = key >= sb.Lk || q0 + 32 > sb.Lq ||
                              (upper && kw + 31 > q0 + off) ||
                              (p.window > 0 && kw < q0 + 31 + off - p.window + 1);
@@ -520,6 +515,15 @@ void bwd_kv_kernel(BwdParams p) {
       u32x4 bk[2];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
+        // lse2 / delta of rows j = 2 t2, 2 t2 + 1 (read when needed: fewer live
+        // registers)
+        f32x4 l2[4], dl[4];
+#pragma unroll
+        for (int j = 2 * t2; j < 2 * t2 + 2; ++j) {
+          l2[j] = *reinterpret_cast<const f32x4*>(wsv + 8 * j + 4 * hl);
+          if constexpr (MODE == MODE_DK)
+            dl[j] = *reinterpret_cast<const f32x4*>(wsv + 32 + 8 * j + 4 * hl);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 8 * t2 + 2 * i;
