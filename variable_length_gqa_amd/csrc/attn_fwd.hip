@@ -382,17 +382,8 @@ void fwd16_kernel(FwdParams p) {
           s[kb] = mfma16<ELEM>(a, qf[ks], s[kb]);
         }
       }
-      // schedule: four K fragment reads in flight ahead of the products (the
-      // default interleave keeps two; +1% measured)
-      if constexpr (NKB == 1) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
-#pragma unroll
-        for (int i = 0; i < C::NS - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      }
+      // four K fragment reads in flight ahead of the products (+1% measured)
+      if constexpr (NKB == 1) sched_lds_ahead<C::NS, 1, 4>();
       const bool need_mask = (c0 + BN > w.Lk) || (upper && c0 + BN - 1 > wa + off) ||
                              (p.window > 0 && c0 < wb + off - p.window + 1);
       if (need_mask) mask_blocks<NKB>(s, c0, hl, qrow, off, w.Lk, upper, p.window);
@@ -455,18 +446,9 @@ void fwd16_kernel(FwdParams p) {
           st.o[db] = mfma16<ELEM>(a, pk[t2], st.o[db]);
         }
       }
-      // schedule: two V^T operands (two transposing reads each) in flight
-      // ahead of the products (+1% measured)
-      if constexpr (NKB == 1) {
-        constexpr int NPV = 2 * C::NOB;  // products of the tile
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < NPV - 2; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      }
+      // two V^T operands (two transposing reads each) in flight ahead of the
+      // products (+1% measured)
+      if constexpr (NKB == 1) sched_lds_ahead<2 * C::NOB, 2, 2>();
     }
     wait_vm_all();  // tile t+1 has landed (this wave's part)
     lds_barrier();  // ... and everyone's
@@ -705,6 +687,7 @@ void fwd8_kernel(FwdParams p) {
           st.o[db] = mfma16<E_BF16>(a, pk[t2], st.o[db]);
         }
       }
+      sched_lds_ahead<2 * C::NOB, 2, 2>();
     }
     wait_vm_all();            // K(t+1) DMA and the V(t+1) codes have landed
     if (more) store_v(vnext, vc);

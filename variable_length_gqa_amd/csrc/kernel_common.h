@@ -129,6 +129,21 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Scheduling hint for the run of N matrix products just emitted, each fed by R
+// LDS reads: keep the reads of AHEAD products in flight ahead of the products
+// (the default interleave issues them just in time).  Only instructions of
+// the current scheduling region take part.
+template <int N, int R, int AHEAD>
+__device__ __forceinline__ void sched_lds_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one product
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);        // its successor's reads
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
 // (lgkmcnt) but lets global loads and LDS DMA stay in flight across it.  A
 // __syncthreads(), and even an LDS-scoped fence, drains every outstanding
