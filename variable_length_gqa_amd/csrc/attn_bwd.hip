@@ -480,6 +480,7 @@ void bwd_kv_kernel(BwdParams p) {
           if constexpr (MODE == MODE_DK)
             dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(dpt + ro), vf[ks][0], dp);
         }
+        sched_lds_ahead<(MODE == MODE_DK ? 2 : 1) * C::NS, 1, 4>();
       } else {
 #pragma unroll
         for (int ks = 0; ks < NSB; ++ks) {
@@ -491,6 +492,7 @@ void bwd_kv_kernel(BwdParams p) {
             dp = mfma_fp8(a, vf[ks], dp);
           }
         }
+        sched_lds_ahead<(MODE == MODE_DK ? 2 : 1) * NSB, 2, 2>();
       }
       // register r holds query row q0 + qq(r) + 4 hl, qq(r) = 8 (r / 4) + r % 4
 
@@ -776,6 +778,7 @@ void bwd_dq_kernel(BwdParams p) {
           sc = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(kb_ + ro), qf[ks][0], sc);
           dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(vb_ + ro), of[ks][0], dp);
         }
+        sched_lds_ahead<2 * C::NS, 1, 4>();
       } else {
 #pragma unroll
         for (int ks = 0; ks < NSB; ++ks) {
@@ -785,6 +788,7 @@ void bwd_dq_kernel(BwdParams p) {
           tile8_read<D>(vb_ + T8, ql, hl, ks, a);
           dp = mfma_fp8(a, of[ks], dp);
         }
+        sched_lds_ahead<2 * NSB, 2, 2>();
       }
       // register r holds key c0 + kk(r) + 4 hl, kk(r) = 8 (r / 4) + r % 4
       const bool need_mask = (c0 + 32 > sb.Lk) || (upper && c0 + 31 > wa + off) ||
