@@ -90,9 +90,25 @@ __device__ __forceinline__ int64_t ws_plane(const BwdParams& p) {
 // ---------------------------------------------------------------------------
 //
 // D/8 lanes per (row, head), 16 bytes of dO and of O each, reduced across
-// those lanes; pairs are (b, h, r) with r fastest, so the lanes that write
-// the head-major workspace write consecutive floats, and each lane group
-// reads whole lines of a row in either layout.
+// those lanes.  Pair order: packed layout (b, r, h) with h fastest, so a wave
+// reads one contiguous stretch of a token's heads; dense layout (b, h, r)
+// with r fastest, which is contiguous in memory and lets the lanes write
+// consecutive floats of the head-major workspace.
+__device__ __forceinline__ void pair_index(const BwdParams& p, int64_t pair, int& b, int& h,
+                                           int64_t& r) {
+  if (p.cu_q) {
+    h = (int)(pair % p.heads);
+    const int64_t rest = pair / p.heads;
+    r = rest % p.d_rows;
+    b = (int)(rest / p.d_rows);
+  } else {
+    r = pair % p.d_rows;
+    const int64_t rest = pair / p.d_rows;
+    h = (int)(rest % p.heads);
+    b = (int)(rest / p.heads);
+  }
+}
+
 template <int ELEM, int D>
 __global__ __launch_bounds__(256) void bwd_rowsum_kernel(BwdParams p) {
   constexpr int LPR = D / 8;
@@ -105,10 +121,7 @@ __global__ __launch_bounds__(256) void bwd_rowsum_kernel(BwdParams p) {
   int h = 0, b = 0;
   int64_t r = 0;
   if (pair < npairs) {
-    r = pair % p.d_rows;
-    const int64_t rest = pair / p.d_rows;
-    h = (int)(rest % p.heads);
-    b = (int)(rest / p.heads);
+    pair_index(p, pair, b, h, r);
     const int64_t off = (int64_t)b * p.q_bs + r * p.q_rs + (int64_t)h * p.q_hs + sub * 8;
     const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.dout) + off);
     const u32x4 c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.o) + off);
@@ -140,10 +153,7 @@ __global__ __launch_bounds__(256) void bwd_rowsum8_kernel(BwdParams p) {
   int h = 0, b = 0;
   int64_t r = 0;
   if (pair < npairs) {
-    r = pair % p.d_rows;
-    const int64_t rest = pair / p.d_rows;
-    h = (int)(rest % p.heads);
-    b = (int)(rest / p.heads);
+    pair_index(p, pair, b, h, r);
     const int64_t off = (int64_t)b * p.q_bs + r * p.q_rs + (int64_t)h * p.q_hs + sub * 16;
     const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.do8) + off);
     const u32x4 c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.o) + off);
