@@ -46,29 +46,48 @@ __global__ __launch_bounds__(kScanThreads) void cu_seqlens_kernel(const int32_t*
   }
 }
 
-// packed row t <- padded row (b, t - cu[b]) with cu[b] <= t < cu[b+1].  IDX is
-// uint32_t when every chunk index fits (cheap division), else int64_t.
-template <typename IDX>
-__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* padded, const int32_t* cu,
-                                                   int64_t batch, int64_t S, int64_t row16_,
-                                                   int64_t total, uint8_t* packed) {
-  const IDX row16 = (IDX)row16_;
-  const IDX n = (IDX)(total * row16_);
-  for (IDX i = (IDX)blockIdx.x * 256 + threadIdx.x; i < n; i += (IDX)gridDim.x * 256) {
-    const IDX t = i / row16, c = i - t * row16;
-    int64_t lo = 0, hi = batch;  // largest b with cu[b] <= t
-    while (hi - lo > 1) {
-      const int64_t mid = (lo + hi) >> 1;
-      if ((IDX)cu[mid] <= t) lo = mid; else hi = mid;
-    }
-    const int64_t s = (int64_t)t - cu[lo];
-    const u32x4 v = *reinterpret_cast<const u32x4*>(
-        padded + ((lo * S + s) * (int64_t)row16 + (int64_t)c) * 16);
-    *reinterpret_cast<u32x4*>(packed + (int64_t)i * 16) = v;
+// Pack: one wave per packed row (grid-stride over rows, wave-uniform, so the
+// sequence lookup runs on the scalar unit once per row); the lanes copy the
+// row's 16-byte chunks with four loads in flight each.  (The same scheme for
+// unpack measured 10% slower than its one-chunk-per-thread form below.)
+__device__ __forceinline__ int64_t wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+}
+
+__device__ __forceinline__ void copy_row(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                         int64_t row16, int lane) {
+  for (int64_t c = lane; c < row16; c += 256) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (c + 64 * j < row16) v[j] = src[c + 64 * j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (c + 64 * j < row16) dst[c + 64 * j] = v[j];
   }
 }
 
-// padded row (b, s) <- packed row cu[b] + s for s < length_b, else zeros
+// packed row t <- padded row (b, t - cu[b]) with cu[b] <= t < cu[b+1]
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ padded,
+                                                   const int32_t* __restrict__ cu, int64_t batch,
+                                                   int64_t S, int64_t row16, int64_t total,
+                                                   uint8_t* __restrict__ packed) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t t = wave_id(); t < total; t += nwaves) {
+    int64_t lo = 0, hi = batch;  // largest b with cu[b] <= t
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (cu[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int64_t s = t - cu[lo];
+    copy_row(reinterpret_cast<const u32x4*>(padded + (lo * S + s) * row16 * 16),
+             reinterpret_cast<u32x4*>(packed + t * row16 * 16), row16, lane);
+  }
+}
+
+// padded row (b, s) <- packed row cu[b] + s for s < length_b, else zeros: one
+// thread per 16-byte chunk (IDX uint32_t when every chunk index fits)
 template <typename IDX>
 __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* packed, const int32_t* cu,
                                                      int64_t batch, int64_t S_, int64_t row16_,
@@ -92,6 +111,12 @@ unsigned grid_for(int64_t n) {
   return (unsigned)(blocks < 65536 ? blocks : 65536);  // grid-stride beyond
 }
 
+// workgroups of 4 one-row waves: enough to cover the rows, at most 8 per CU
+unsigned grid_for_rows(int64_t rows) {
+  const int64_t blocks = (rows + 3) / 4;
+  return (unsigned)(blocks < 2048 ? blocks : 2048);
+}
+
 }  // namespace
 
 hipError_t launch_cu_seqlens(const int32_t* lengths, int64_t batch, int32_t* cu,
@@ -103,19 +128,10 @@ hipError_t launch_cu_seqlens(const int32_t* lengths, int64_t batch, int32_t* cu,
 
 hipError_t launch_pack(const void* padded, const int32_t* cu, int64_t batch, int64_t S,
                        int64_t row_bytes, int64_t total, void* packed, hipStream_t stream) {
-  const int64_t row16 = row_bytes / 16;
-  const int64_t n = total * row16;
-  const bool small = n + (int64_t)65536 * 256 < ((int64_t)1 << 32);
-  if (n > 0) {
-    if (small)
-      hipLaunchKernelGGL(pack_kernel<uint32_t>, dim3(grid_for(n)), dim3(256), 0, stream,
-                         reinterpret_cast<const uint8_t*>(padded), cu, batch, S, row16, total,
-                         reinterpret_cast<uint8_t*>(packed));
-    else
-      hipLaunchKernelGGL(pack_kernel<int64_t>, dim3(grid_for(n)), dim3(256), 0, stream,
-                         reinterpret_cast<const uint8_t*>(padded), cu, batch, S, row16, total,
-                         reinterpret_cast<uint8_t*>(packed));
-  }
+  if (total > 0)
+    hipLaunchKernelGGL(pack_kernel, dim3(grid_for_rows(total)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint8_t*>(padded), cu, batch, S, row_bytes / 16,
+                       total, reinterpret_cast<uint8_t*>(packed));
   return hipGetLastError();
 }
 
