@@ -1,7 +1,7 @@
 """GPU parity at sizes beyond the named workloads: one 131072-token sequence
 (query and key indices past 2^16, 1024 query tiles, 4096 key tiles) and a
 262144-key KV cache for the decode path, on rows the oracle computes one by
-one."""
+one; and the other extreme, 500 sequences of 0-40 tokens."""
 
 import numpy as np
 import pytest
@@ -52,3 +52,30 @@ def test_decode_262144_key_cache():
     to, tl = TOL[torch.bfloat16]
     assert_close("O", to_f64(o.cpu()), O, to, torch.bfloat16)
     assert_close("LSE", l.cpu().double().numpy(), L, tl)
+
+
+def test_many_tiny_sequences_forward_and_backward():
+    """500 sequences of 0-40 tokens (many empty or shorter than one tile) and
+    a group of 16 query heads per kv head: forward and backward against the
+    oracle on every element."""
+    g = torch.Generator().manual_seed(704)
+    lengths = [int(n) for n in torch.randint(0, 41, (500,), generator=g)]
+    x = W.make_varlen(lengths, num_heads=16, num_kv_heads=1, head_dim=64, dtype=torch.bfloat16,
+                      causal=True, seed=705)
+    xd = x.to(DEV)
+    B, mx = len(lengths), max(lengths)
+    o, l = vg.varlen_attention_fwd(xd.q, xd.k, xd.v, xd.cu_q, xd.cu_k, B, 16, 1, mx, mx, 64, True)
+    dO = W.make_dout(x.q, 706)
+    dq, dk, dv = vg.varlen_attention_bwd(dO.to(DEV), xd.q, xd.k, xd.v, o, l, xd.cu_q, xd.cu_k, B,
+                                         16, 1, mx, mx, 64, True)
+    torch.cuda.synchronize()
+    O, L = oracle.varlen_attention_fwd(x.q, x.k, x.v, x.cu_q, x.cu_k, 16, 1, True,
+                                       workers=oracle_workers())
+    to, tl = TOL[torch.bfloat16]
+    assert_close("O", to_f64(o.cpu()), O, to, torch.bfloat16)
+    assert_close("LSE", l.cpu().double().numpy(), L, tl)
+    refs = oracle.varlen_attention_bwd(dO, x.q, x.k, x.v, x.cu_q, x.cu_k, 16, 1, True,
+                                       workers=oracle_workers())
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        err = float(np.abs(to_f64(got.cpu()) - ref).max())
+        assert err <= 1.5e-2 * float(np.abs(ref).max()), (name, err)
