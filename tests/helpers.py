@@ -106,3 +106,26 @@ def nan_like(t: torch.Tensor) -> torch.Tensor:
     if t.dtype == torch.uint8:
         return torch.full_like(t, 0x7F)
     return torch.full_like(t, math.nan)
+
+
+def f16_large_probability_case(num_heads=4, seqlen_q=8, seed=0):
+    """Dense f16 input whose second 32-key tile holds one key scoring 15.99976
+    (log2 units, after the 1/sqrt(128) scale) above the first tile's maximum:
+    exp2 of it is 65525, which rounds past the largest finite f16 (65504), while
+    the row's running sum of probabilities stays below 2^16.  Keys 0-31 score 0,
+    key 32 scores 124.5 + 1989/2048 (exact in f32), keys 33-63 score -128.  One KV
+    head, non-causal, 64 keys."""
+    g = torch.Generator().manual_seed(seed)
+    D = 128
+    q = torch.zeros(1, num_heads, seqlen_q, D)
+    q[..., 0] = 1.0
+    q[..., 1] = 1.0
+    k = torch.zeros(1, 1, 64, D)
+    k[0, 0, 32, 0] = 124.5
+    k[0, 0, 32, 1] = 1989 / 2048  # exact in f16
+    k[0, 0, 33:, :2] = -64.0
+    v = torch.randn(1, 1, 64, D, generator=g)
+    assert float(k[0, 0, 32, :2].half().float().sum()) == 124.5 + 1989 / 2048
+    from variable_length_gqa_amd.workloads import Dense
+    return Dense(q.half(), k.half(), v.half(), num_heads, 1, D, False, 0, None,
+                 "f16-large-probability")

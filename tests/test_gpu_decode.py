@@ -14,7 +14,7 @@ import oracle
 import variable_length_gqa_amd as vg
 from variable_length_gqa_amd import workloads as W
 
-from .helpers import TOL, assert_close, oracle_workers, to_f64
+from .helpers import TOL, assert_close, f16_large_probability_case, oracle_workers, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -112,3 +112,12 @@ def test_decode_workload_full_size():
     8192 cached keys in a 16384-slot buffer), every head against the oracle."""
     d = W.workload("dense_bf16_decode")
     check_decode(d)
+
+
+@pytest.mark.parametrize("seqlen_q", [1, 8])
+def test_decode_f16_probability_beyond_f16_range(seqlen_q):
+    """The decode tile loop under the same large-probability row as the forward:
+    one key just under 2^16 times the reference after a first tile of zeros."""
+    d = f16_large_probability_case(num_heads=4, seqlen_q=seqlen_q, seed=116)
+    o, _ = check_decode(d)
+    assert torch.isfinite(o).all()

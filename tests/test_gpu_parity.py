@@ -12,8 +12,8 @@ import oracle
 import variable_length_gqa_amd as vg
 from variable_length_gqa_amd import workloads as W
 
-from .helpers import FP8_LSE_TOL, FP8_REL_TOL, TOL, assert_close, e4m3_decode_torch, nan_like, \
-    to_f64
+from .helpers import FP8_LSE_TOL, FP8_REL_TOL, TOL, assert_close, e4m3_decode_torch, \
+    f16_large_probability_case, nan_like, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -120,6 +120,16 @@ def test_causal_first_row_is_v0_bit_exact(dtype):
         s = int(x.cu_q[b])
         for h in range(8):
             assert torch.equal(o[s, h], x.v[s, h // 4]), (b, h)
+
+
+@pytest.mark.parametrize("seqlen_q", [1, 8, 130])
+def test_f16_probability_beyond_f16_range(seqlen_q):
+    """A later tile raises a row's score to just under 2^16 times the running
+    reference: the probability must not be rounded to f16 unchecked (it would
+    become inf and O NaN)."""
+    d = f16_large_probability_case(num_heads=4, seqlen_q=seqlen_q, seed=115)
+    o, _ = check_dense(d)
+    assert torch.isfinite(o).all()
 
 
 def test_deterministic():

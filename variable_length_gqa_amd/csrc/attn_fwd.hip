@@ -40,9 +40,10 @@ namespace vlgqa {
 // this (log2 units); until then probabilities may reach 2^kRescaleSlack.  The
 // result is exact either way: numerator and denominator use the same reference.
 constexpr float kRescaleSlack = 8.0f;
-// bf16/f16 kernel: a lane's partial sum of probabilities (32 of them) may
-// reach this before the reference maximum is moved (probabilities <= 2^16).
-constexpr float kPartialSumBound = 65536.0f;
+// bf16/f16 kernels: a lane's partial sum of a tile's probabilities may reach
+// this before the reference maximum is moved.  It also bounds each probability,
+// and 2^15 keeps every one finite in f16 (largest finite value 65504).
+constexpr float kPartialSumBound = 32768.0f;
 
 // ---------------------------------------------------------------------------
 // work decode: XCD-aware, longest query tiles first
@@ -388,9 +389,9 @@ void fwd16_kernel(FwdParams p) {
                              (p.window > 0 && c0 < wb + off - p.window + 1);
       if (need_mask) mask_blocks<NKB>(s, c0, hl, qrow, off, w.Lk, upper, p.window);
 
-      // Online softmax over the row's 64 scores (32 here, 32 in lane ^ 32).
+      // Online softmax over the row's BN scores (half here, half in lane ^ 32).
       // Optimistic: exponentiate against the current reference maximum and
-      // move the reference only when some lane's partial sum exceeds 2^16
+      // move the reference only when some lane's partial sum exceeds 2^15
       // (or is not finite) -- the first tile of a row, or a large jump.  Then
       // the true tile maximum is taken, O and l are rescaled and the tile is
       // exponentiated again.  Any reference gives the exact result (numerator

@@ -27,7 +27,10 @@ namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kDecPartialBound = 65536.0f;
+// a lane's partial sum of a tile's probabilities may reach this before the
+// reference maximum is moved; it also bounds each probability, and 2^15 keeps
+// every one finite in f16 (largest finite value 65504)
+constexpr float kDecPartialBound = 32768.0f;
 constexpr int kMaxDecodeParts = 256;
 
 // s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left at their maxima
