@@ -323,13 +323,14 @@ __device__ __forceinline__ void store_rows_e4m3(void* base, int64_t row_off, int
 // dK and dV
 // ---------------------------------------------------------------------------
 //
-// Two launches of one kernel body, so that each fits at least two waves per
-// SIMD: MODE_DV computes S -> P -> dV^T += dO^T P (K^T of the lane's key in
-// registers, dV^T accumulators), MODE_DK computes S, dP -> dS -> dK^T +=
-// Q^T dS (K^T and V^T in registers, dK^T accumulators).  S is recomputed by
-// both (10 D + 2 D FLOPs per pair in the two launches instead of 8 D fused),
-// which costs less than running one fused kernel at one wave per SIMD.
-enum : int { MODE_DV = 0, MODE_DK = 1 };
+// One kernel body, three modes.  MODE_DKV (16-bit inputs) computes S, dP ->
+// P, dS -> dV^T += dO^T P and dK^T += Q^T dS in one pass: K^T of the lane's
+// key in registers, V of the workgroup's 128 keys in LDS (read as the B
+// operand of dP each stage), both accumulators in registers (two waves per
+// SIMD at D = 128).  MODE_DV (S -> P -> dV^T) and MODE_DK (S, dP -> dS ->
+// dK^T, K^T and V^T in registers) are two launches of the E4M3 path, whose
+// FP8 operands do not leave room for the fused body.
+enum : int { MODE_DV = 0, MODE_DK = 1, MODE_DKV = 2 };
 
 // E8: E4M3 inputs.  S = Q K^T (and dP = dO V^T) run on the FP8 matrix cores
 // from the codes (K^T / V^T codes in registers, Q / dO code tiles in LDS); the
@@ -340,6 +341,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                               MODE == MODE_DV || E8 || D == 64 ? 3 : 2)))
 void bwd_kv_kernel(BwdParams p) {
   using C = T16<D>;
+  constexpr bool FUSED = MODE == MODE_DKV;
+  static_assert(!(FUSED && E8), "the fused body takes 16-bit inputs");
   constexpr int T8 = 32 * D;  // bytes of an E4M3 tile
   // stage buffer (byte offsets): the S operand tile, the dP operand tile (dK),
   // the transposed-read tile of the accumulation, then 32 lse2 + 32 delta
@@ -349,7 +352,9 @@ void bwd_kv_kernel(BwdParams p) {
   constexpr int OFF_T = !E8 ? (MODE == MODE_DV ? C::TILE : 0) : (MODE == MODE_DV ? T8 : 2 * T8);
   constexpr int OFF_W = !E8 ? 2 * C::TILE : (MODE == MODE_DV ? T8 + C::TILE : 2 * T8 + C::TILE);
   constexpr int STAGE = OFF_W + 256;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  // fused: V rows of the workgroup's keys after the two stages (4 tiles)
+  constexpr int OFF_V = 2 * STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE + (FUSED ? 4 * C::TILE : 0)];
 
   // work: a "stream" is (batch, kv head, split) -- the query heads whose Q /
   // dO it reads; one split covers group / n_split query heads.  Blocks go to
@@ -403,10 +408,24 @@ void bwd_kv_kernel(BwdParams p) {
         if constexpr (MODE == MODE_DK) vf[ks][c] = bload16(vr, o);
       }
     }
+    if constexpr (FUSED) {
+      // V rows k0 .. k0 + 127 into LDS in the tile layout (rows past the
+      // sequence arrive as zeros); awaited with the first stage
+      uint32_t voffk[C::CPT];
+      tile_dma_offsets<D>(voffk, wid, lane, (uint32_t)(p.k_rs * 2));
+      const u32x4 vrw = rsrc_words(vbase + koff, bytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dma_tile16<D>(lds + OFF_V + i * C::TILE, vrw, (uint32_t)(k0 + 32 * i) * (uint32_t)(p.k_rs * 2),
+                      wid, voffk);
+    }
   }
-  f32x16 acc[C::NOB];
+  // accumulators: dV^T (MODE_DV), dK^T (MODE_DK), both (fused: acc = dK^T)
+  f32x16 acc[C::NOB], accv[FUSED ? C::NOB : 1];
 #pragma unroll
   for (int i = 0; i < C::NOB; ++i) acc[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < (FUSED ? C::NOB : 1); ++i) accv[i] = f32x16{};
 
   // query rows that see any key of the workgroup / of this wave
   const int k1 = min(k0 + kTileB, sb.Lk);
@@ -483,7 +502,17 @@ void bwd_kv_kernel(BwdParams p) {
       const uint8_t* dpt = sbuf + OFF_DP;   // A operand of dP (dO rows)
       const float* wsv = reinterpret_cast<const float*>(sbuf + OFF_W);
       f32x16 sc = {}, dp = {};
-      if constexpr (!E8) {
+      if constexpr (FUSED) {
+        // B operand of dP: V^T of the wave's keys, the same row reads as Q
+        const uint8_t* vk = lds + OFF_V + wid * C::TILE;
+#pragma unroll
+        for (int ks = 0; ks < C::NS; ++ks) {
+          const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
+          sc = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(st_ + ro), kf[ks][0], sc);
+          dp = mfma16<ELEM>(*reinterpret_cast<const u32x4*>(dpt + ro),
+                            *reinterpret_cast<const u32x4*>(vk + ro), dp);
+        }
+      } else if constexpr (!E8) {
 #pragma unroll
         for (int ks = 0; ks < C::NS; ++ks) {
           const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
@@ -524,8 +553,9 @@ void bwd_kv_kernel(BwdParams p) {
           if (!kin || qq < lo || qq > hi) sc[r] = -INFINITY;
         }
       }
-      // B operand of the accumulation: P (dV) or dS (dK), 16-bit
-      u32x4 bk[2];
+      // B operand of the accumulation: P (dV) or dS (dK), 16-bit; fused: dS
+      // in bk, P in bp
+      u32x4 bk[2], bp[FUSED ? 2 : 1];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         // lse2 / delta of rows j = 2 t2, 2 t2 + 1 (read when needed: fewer live
@@ -534,7 +564,7 @@ void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
         for (int j = 2 * t2; j < 2 * t2 + 2; ++j) {
           l2[j] = *reinterpret_cast<const f32x4*>(wsv + 8 * j + 4 * hl);
-          if constexpr (MODE == MODE_DK)
+          if constexpr (MODE != MODE_DV)
             dl[j] = *reinterpret_cast<const f32x4*>(wsv + 32 + 8 * j + 4 * hl);
         }
 #pragma unroll
@@ -548,6 +578,7 @@ void bwd_kv_kernel(BwdParams p) {
           else
             bk[t2][i] = pack2<ELEM>(p0 * __builtin_fmaf(dp[r], dpm, -dl[j][e]),
                                     p1 * __builtin_fmaf(dp[r + 1], dpm, -dl[j][e + 1]));
+          if constexpr (FUSED) bp[t2][i] = pack2<ELEM>(p0, p1);
         }
       }
       // dV^T += dO^T P  or  dK^T += Q^T dS  (A by transposing reads)
@@ -558,6 +589,8 @@ void bwd_kv_kernel(BwdParams p) {
         for (int db = 0; db < C::NOB; ++db) {
           const uint32_t o0 = troff[db][0] + t2 * 16 * C::ROWB, o1 = troff[db][1] + t2 * 16 * C::ROWB;
           acc[db] = mfma16<ELEM>(vt_operand(at + o0, at + o1), bk[t2], acc[db]);
+          if constexpr (FUSED)  // dV^T from the dO tile
+            accv[db] = mfma16<ELEM>(vt_operand(dpt + o0, dpt + o1), bp[t2], accv[db]);
         }
       }
     }
@@ -573,19 +606,23 @@ void bwd_kv_kernel(BwdParams p) {
         store_rows<ELEM, D>(p.dv, row, hl, acc, p.dv_mul);
       else
         store_rows<ELEM, D>(p.dk, row, hl, acc, p.dk_mul);
+      if constexpr (FUSED) store_rows<ELEM, D>(p.dv, row, hl, accv, p.dv_mul);
     } else {
-      // f32 partial of this split: [mode][sp][kp_row][kvh][d]
+      // f32 partials of this split: [mode][sp][kp_row][kvh][d], mode 0 dK, 1 dV
       const int64_t kp = (p.cu_k ? 0 : (int64_t)b * p.seqlen_k) + sb.k_start + key;
-      float* dst = p.part + ((((int64_t)(MODE == MODE_DV) * p.n_split + sp) * p.kp_rows + kp) *
-                             p.kv_heads + kvh) * D;
+      auto put = [&](int mode, const f32x16 (&a)[C::NOB]) __attribute__((always_inline)) {
+        float* dst = p.part + ((((int64_t)mode * p.n_split + sp) * p.kp_rows + kp) *
+                               p.kv_heads + kvh) * D;
 #pragma unroll
-      for (int db = 0; db < C::NOB; ++db)
+        for (int db = 0; db < C::NOB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v4 = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2],
-                            acc[db][4 * g + 3]};
-          *reinterpret_cast<f32x4*>(dst + db * 32 + g * 8 + 4 * hl) = v4;
-        }
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v4 = {a[db][4 * g], a[db][4 * g + 1], a[db][4 * g + 2], a[db][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(dst + db * 32 + g * 8 + 4 * hl) = v4;
+          }
+      };
+      put(MODE == MODE_DV ? 1 : 0, acc);
+      if constexpr (FUSED) put(1, accv);
     }
   }
 }
@@ -886,6 +923,17 @@ BwdWorkspace bwd_workspace(int64_t rows, int64_t keys, int64_t heads, int64_t kv
   return w;
 }
 
+// dK and dV: one fused launch for 16-bit inputs, dV then dK for E4M3
+template <int E, int D, int E8>
+void launch_kv(dim3 grid, dim3 blk, hipStream_t stream, const BwdParams& p) {
+  if constexpr (E8) {
+    hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DV, 1>), grid, blk, 0, stream, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DK, 1>), grid, blk, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DKV, 0>), grid, blk, 0, stream, p);
+  }
+}
+
 hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t stream) {
   const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
   const int ppb = 4 * (64 / (head_dim / (p.e4m3 ? 16 : 8)));
@@ -914,8 +962,7 @@ hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t st
   do {                                                                         \
     if (pairs > 0 && !E8)                                                      \
       hipLaunchKernelGGL((bwd_rowsum_kernel<E, D>), g0, blk, 0, stream, p);    \
-    if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DV, E8>), g1, blk, 0, stream, p); \
-    if (g1.x > 0) hipLaunchKernelGGL((bwd_kv_kernel<E, D, MODE_DK, E8>), g1, blk, 0, stream, p); \
+    if (g1.x > 0) launch_kv<E, D, E8>(g1, blk, stream, p);                    \
     if (g2.x > 0) hipLaunchKernelGGL((bwd_dq_kernel<E, D, E8>), g2, blk, 0, stream, p);     \
     if (reduce && g3.x > 0)                                                              \
       hipLaunchKernelGGL((bwd_reduce_kernel<E, D>), g3, blk, 0, stream, p);              \
