@@ -12,16 +12,17 @@
 //   dq_i  = scale sum_j dS_ij k_j,       dk_j = scale sum_i dS_ij q_i
 // with dk / dv of a kv head summed over its G query heads.
 //
-// Four launches (five with the dK / dV reduction, more for E4M3 inputs):
+// Three launches (four with the dK / dV reduction, more for E4M3 inputs):
 //   bwd_rowsum_kernel  delta_i = dO_i.O_i and LSE_i log2(e) per (row, head),
 //                      written head-major into the caller's workspace (so a
 //                      query tile's values are contiguous).
-//   bwd_kv_kernel      dV, then dK (two launches of one body): one workgroup
-//                      per (sequence, kv head, 128-key tile), 4 waves x 32
-//                      keys; K (and V) of the wave's keys stay in registers;
-//                      the loop runs over the G query heads and the 32-row
-//                      query tiles that see the keys, with Q, dO and the
-//                      tile's LSE / delta brought to LDS by DMA (double
+//   bwd_kv_kernel      dK and dV in one pass (E4M3: dV, then dK, two
+//                      launches of one body): one workgroup per (sequence,
+//                      kv head, 128-key tile), 4 waves x 32 keys; K of the
+//                      wave's keys stays in registers, V in LDS (E4M3: both
+//                      in registers); the loop runs over the G query heads and
+//                      the 32-row query tiles that see the keys, with Q, dO
+//                      and the tile's LSE / delta brought to LDS by DMA (double
 //                      buffered).  dV / dK accumulate in registers: no
 //                      atomics, deterministic.
 //   bwd_dq_kernel      one workgroup per (sequence, 128-row query tile, query
@@ -31,7 +32,7 @@
 // Matrix-core formulation (v_mfma_f32_32x32x16_{bf16,f16}): every product has
 // the operand layouts of the forward kernel.  In dK/dV the lane owns a key:
 //   S  = Q K^T     A = Q rows (LDS), B = K^T (registers)  -> lane: key l % 32,
-//   dP = dO V^T    A = dO rows (LDS), B = V^T (registers)    16 query rows
+//   dP = dO V^T    A = dO rows (LDS), B = V^T (LDS rows)     16 query rows
 //   dV^T += dO^T P     A = dO^T by transposing LDS reads, B = P (bf16)
 //   dK^T += Q^T dS     A = Q^T by transposing LDS reads,  B = dS (bf16)
 // In dQ the lane owns a query:
@@ -358,14 +359,15 @@ void bwd_kv_kernel(BwdParams p) {
 
   // work: a "stream" is (batch, kv head, split) -- the query heads whose Q /
   // dO it reads; one split covers group / n_split query heads.  Blocks go to
-  // the 8 XCDs round-robin; stream i always lands on XCD i % 8 (its key tiles
-  // share that XCD's L2), and each XCD runs its key tiles in ascending order
-  // (more queries see the early keys of a causal sequence: longest first).
+  // the 8 XCDs round-robin; stream i always lands on XCD i % 8, and an XCD
+  // runs one stream's key tiles on consecutive slots (ascending: more queries
+  // see the early keys of a causal sequence), so that they are resident
+  // together and read each Q / dO tile from that XCD's L2 at about the same
+  // time.
   const int nstream = p.batch * p.kv_heads * p.n_split;
-  const int per_xcd = (nstream + 7) / 8;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int kt = slot / per_xcd;
-  const int stream = (slot % per_xcd) * 8 + xcd;
+  const int kt = slot % p.n_ktiles;
+  const int stream = (slot / p.n_ktiles) * 8 + xcd;
   if (stream >= nstream) return;
   const int sp = stream % p.n_split;
   const int kvh = (stream / p.n_split) % p.kv_heads;
@@ -433,9 +435,10 @@ void bwd_kv_kernel(BwdParams p) {
   const int qb = p.window > 0 ? min(sb.Lq, k1 - 1 - off + p.window) : sb.Lq;
   const int ta = qa / 32, tb = qb > qa ? (qb + 31) / 32 : ta;
   const int nt = tb - ta;
-  // stages: (query head, query tile), the tiles from the last one down, so
-  // that the workgroups of one stream (which start at different tiles under a
-  // causal mask) read the same Q / dO tiles at about the same time
+  // stages: (query tile, query head), the tiles from the last one down and
+  // the heads inside a tile, so that the workgroups of one stream (whose
+  // tile ranges differ at the low end under a causal mask) read the same
+  // Q / dO tiles at the same stage index for as long as they run
   const int nst = nt * gsplit;
   const int kw1 = min(kw + 32, sb.Lk);
   const bool wave_keys = kw < sb.Lk;
@@ -453,7 +456,7 @@ void bwd_kv_kernel(BwdParams p) {
 
   // DMA of stage s into buffer u: the tiles of (head, tile) and its lse2/delta
   auto issue = [&](int s, int u) __attribute__((always_inline)) {
-    const int hh = s / nt, t = tb - 1 - s % nt;
+    const int hh = s % gsplit, t = tb - 1 - s / gsplit;
     const int h = hbase + hh;
     const int64_t qrow0 = (int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs + (int64_t)h * p.q_hs;
     const uint32_t bytes = sat_bytes((int64_t)sb.Lq * p.q_rs * 2);
@@ -494,7 +497,7 @@ void bwd_kv_kernel(BwdParams p) {
   for (int s = 0; s < nst; ++s) {
     const int u = s & 1;
     if (s + 1 < nst) issue(s + 1, u ^ 1);
-    const int t = tb - 1 - s % nt;
+    const int t = tb - 1 - s / gsplit;
     const int q0 = t * 32;
     if (wave_keys && q0 < wqb && q0 + 32 > wqa) {
       const uint8_t* sbuf = lds + u * STAGE;
