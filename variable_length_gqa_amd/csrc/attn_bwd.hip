@@ -694,7 +694,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
 // (Q^T / dO^T codes in registers, K / V code tiles in LDS, in the second half
 // of the lv buffers); dQ^T += K^T dS^T keeps the bf16 copy of the K tile.
 template <int ELEM, int D, int E8>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 void bwd_dq_kernel(BwdParams p) {
   using C = T16<D>;
   constexpr int T8 = 32 * D;  // bytes of an E4M3 tile

@@ -884,7 +884,8 @@ bool plan_fwd(FwdParams& p, int elem, int head_dim) {
 #define VLGQA_WPE 3
 #endif
 constexpr int kNkb = VLGQA_NKB;  // 32-key blocks per tile of the bf16/f16 kernel
-constexpr int kWpe = VLGQA_WPE;  // its waves per SIMD
+constexpr int kWpe = VLGQA_WPE;  // its waves per SIMD (D = 128)
+constexpr int kWpe64 = 4;        // at D = 64 (about 100 VGPRs, 16 KB of LDS a workgroup)
 
 hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t stream) {
   const int64_t grid = fwd_grid_size(p);
@@ -901,8 +902,8 @@ hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t st
     }
   } else if (head_dim == 64) {
     switch (elem) {
-      case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 64, kNkb, kWpe>)); break;
-      case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 64, kNkb, kWpe>)); break;
+      case E_BF16: VLGQA_LAUNCH((fwd16_kernel<E_BF16, 64, kNkb, kWpe64>)); break;
+      case E_F16: VLGQA_LAUNCH((fwd16_kernel<E_F16, 64, kNkb, kWpe64>)); break;
       case E_E4M3: VLGQA_LAUNCH((fwd8_kernel<64>)); break;
       case E_F32: VLGQA_LAUNCH((fwd32_kernel<64>)); break;
       default: return hipErrorInvalidValue;
