@@ -359,15 +359,17 @@ void bwd_kv_kernel(BwdParams p) {
 
   // work: a "stream" is (batch, kv head, split) -- the query heads whose Q /
   // dO it reads; one split covers group / n_split query heads.  Blocks go to
-  // the 8 XCDs round-robin; stream i always lands on XCD i % 8, and an XCD
-  // runs one stream's key tiles on consecutive slots (ascending: more queries
-  // see the early keys of a causal sequence), so that they are resident
-  // together and read each Q / dO tile from that XCD's L2 at about the same
-  // time.
+  // the 8 XCDs round-robin and stream i always lands on XCD i % 8.  When a
+  // stream's Q / dO exceed an XCD's L2 (stream_major), an XCD runs one
+  // stream's key tiles on consecutive slots, so that they are resident
+  // together and read each Q / dO tile from L2 at about the same time;
+  // otherwise it runs the streams' first key tiles first (longest work
+  // first under a causal mask).  Key tiles ascend in both orders.
   const int nstream = p.batch * p.kv_heads * p.n_split;
+  const int per_xcd = (nstream + 7) / 8;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int kt = slot % p.n_ktiles;
-  const int stream = (slot / p.n_ktiles) * 8 + xcd;
+  const int kt = p.stream_major ? slot % p.n_ktiles : slot / per_xcd;
+  const int stream = (p.stream_major ? slot / p.n_ktiles : slot % per_xcd) * 8 + xcd;
   if (stream >= nstream) return;
   const int sp = stream % p.n_split;
   const int kvh = (stream / p.n_split) % p.kv_heads;
@@ -912,6 +914,9 @@ bool plan_bwd(BwdParams& p, int head_dim) {
   if ((nq * p.batch * p.kv_heads + 8) * p.group > INT32_MAX / 2) return false;
   p.n_ktiles = (int32_t)nk;
   p.n_qtiles = (int32_t)nq;
+  // the Q and dO bytes one dK/dV stream reads, against the 4 MiB L2 of an XCD
+  const int64_t stream_bytes = (int64_t)p.max_seqlen_q * (p.group / p.n_split) * head_dim * 2 * 2;
+  p.stream_major = stream_bytes >= ((int64_t)4 << 20) ? 1 : 0;
   const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
   return pairs / (4 * (64 / (head_dim / 8))) < INT32_MAX / 2;
 }

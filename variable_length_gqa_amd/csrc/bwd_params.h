@@ -39,6 +39,8 @@ struct BwdParams {
   // filled by plan_bwd:
   int32_t n_split;    // workgroups per (kv head, key tile): 1 or 2
   int32_t n_ktiles;   // ceil(max_seqlen_k / 128): key tiles of the dK/dV kernel
+  int32_t stream_major;  // dK/dV block order: one stream's key tiles together (1) or
+                         // the streams' first key tiles first (0)
   int32_t n_qtiles;   // ceil(max_seqlen_q / 128): query tiles of the dQ kernel
   float score_mul;    // log2(e) / sqrt(D): scores into the log2 domain
   float scale;        // 1 / sqrt(D)
