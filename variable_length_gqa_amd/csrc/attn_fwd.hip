@@ -185,6 +185,49 @@ __device__ __forceinline__ void store_row(const FwdParams& p, const Work& w, int
   }
 }
 
+// 16-bit output through LDS: the wave writes its normalised 32 x D tile of O
+// into `stage` (its own 32 * 2D bytes, rows with their 16-byte chunks
+// XOR-swizzled by row as in the K/V tiles), then reads it back a row chunk
+// per lane and stores whole rows: 16-byte stores covering 64 / (D / 8) rows
+// each, in place of 8-byte stores scattered over 32 rows.  LSE as store_row.
+template <int OUT_ELEM, int D>
+__device__ __forceinline__ void store_row_staged(const FwdParams& p, const Work& w, int h,
+                                                 int r0w, int ql, int hl, float m, float l,
+                                                 const f32x16 (&o)[D / 32], uint8_t* stage) {
+  static_assert(OUT_ELEM == E_BF16 || OUT_ELEM == E_F16, "16-bit output");
+  constexpr int ROWB = 2 * D, CPR = ROWB / 16;
+  const float ltot = swap_halves_sum(l);
+  const float inv = ltot > 0.0f ? p.out_mul / ltot : 0.0f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // d = 32 db + 8 g + 4 hl .. +4: half of logical chunk 4 db + g
+      const int c = 4 * db + g;
+      const u32x2 v = {pack2<OUT_ELEM>(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
+                       pack2<OUT_ELEM>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+      *reinterpret_cast<u32x2*>(stage + ql * ROWB + ((c ^ swz<D>(ql)) * 16) + 8 * hl) = v;
+    }
+  }
+  const int qrow = r0w + ql;
+  if (hl == 0 && qrow < w.Lq) {
+    const float lse = ltot > 0.0f ? (m + __builtin_log2f(ltot)) * kLn2 : -INFINITY;
+    p.lse[(int64_t)w.b * p.l_bs + (int64_t)(w.q_start + qrow) * p.l_rs + (int64_t)h * p.l_hs] = lse;
+  }
+  const int lane = ql + 32 * hl;
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int row = RPI * k + lane / CPR, c = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * ROWB + ((c ^ swz<D>(row)) * 16));
+    if (r0w + row < w.Lq) {
+      const int64_t orow = (int64_t)w.b * p.o_bs + (int64_t)(w.q_start + r0w + row) * p.o_rs +
+                           (int64_t)h * p.o_hs;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.o) + orow + 8 * c) = v;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 / f16 kernel
 // ---------------------------------------------------------------------------
@@ -462,7 +505,11 @@ void fwd16_kernel(FwdParams p) {
   }
   if (t < t1) tile(t, lk0, lv0, lk1, lv1);
 
-  store_row<OUT, D>(p, w, h, qrow, hl, st.m, st.l, st.o);
+  // every wave has passed the last tile's barrier (or the prologue's): the
+  // four K/V buffers are free, one per wave, each the size of its O tile
+  static_assert(C::TILE == 32 * 2 * D, "a K/V buffer holds one wave's O tile");
+  uint8_t* stage = wid == 0 ? lk0 : wid == 1 ? lk1 : wid == 2 ? lv0 : lv1;
+  store_row_staged<OUT, D>(p, w, h, w.r0 + 32 * wid, ql, hl, st.m, st.l, st.o, stage);
 }
 
 // ---------------------------------------------------------------------------
