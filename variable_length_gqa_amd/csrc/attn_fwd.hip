@@ -228,6 +228,47 @@ __device__ __forceinline__ void store_row_staged(const FwdParams& p, const Work&
   }
 }
 
+// The same for E4M3 output: the wave's 32 x D tile of codes (rows of D bytes,
+// 16-byte chunks XOR-swizzled by swz8) goes through `stage` (32 * D bytes),
+// and whole rows are stored with 16-byte stores.
+template <int D>
+__device__ __forceinline__ void store_row_staged8(const FwdParams& p, const Work& w, int h,
+                                                  int r0w, int ql, int hl, float m, float l,
+                                                  const f32x16 (&o)[D / 32], uint8_t* stage) {
+  constexpr int CPR = D / 16;
+  const float ltot = swap_halves_sum(l);
+  const float inv = ltot > 0.0f ? p.out_mul / ltot : 0.0f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // codes d = 32 db + 8 g + 4 hl .. +4: bytes 8 (g % 2) + 4 hl of chunk 2 db + g / 2
+      const int c = 2 * db + (g >> 1);
+      const uint32_t v = pack4_fp8(sat448(o[db][4 * g + 0] * inv), sat448(o[db][4 * g + 1] * inv),
+                                   sat448(o[db][4 * g + 2] * inv), sat448(o[db][4 * g + 3] * inv));
+      *reinterpret_cast<uint32_t*>(stage + ql * D + ((c ^ swz8<D>(ql)) * 16) + 8 * (g & 1) +
+                                   4 * hl) = v;
+    }
+  }
+  const int qrow = r0w + ql;
+  if (hl == 0 && qrow < w.Lq) {
+    const float lse = ltot > 0.0f ? (m + __builtin_log2f(ltot)) * kLn2 : -INFINITY;
+    p.lse[(int64_t)w.b * p.l_bs + (int64_t)(w.q_start + qrow) * p.l_rs + (int64_t)h * p.l_hs] = lse;
+  }
+  const int lane = ql + 32 * hl;
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int row = RPI * k + lane / CPR, c = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * D + ((c ^ swz8<D>(row)) * 16));
+    if (r0w + row < w.Lq) {
+      const int64_t orow = (int64_t)w.b * p.o_bs + (int64_t)(w.q_start + r0w + row) * p.o_rs +
+                           (int64_t)h * p.o_hs;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(p.o) + orow + 16 * c) = v;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 / f16 kernel
 // ---------------------------------------------------------------------------
@@ -749,7 +790,11 @@ void fwd8_kernel(FwdParams p) {
   }
   if (t < t1) tile(t, lk0, lv0, lk1, lv1);
 
-  store_row<E_E4M3, D>(p, w, h, qrow, hl, st.m, st.l, st.o);
+  // every wave has passed the last tile's barrier: the K (32 D bytes each)
+  // and V (64 D bytes each) buffers are free, one per wave
+  static_assert(C::KTILE >= 32 * D && C::VTILE >= 32 * D, "a buffer holds a wave's O codes");
+  uint8_t* stage = wid == 0 ? lk0 : wid == 1 ? lk1 : wid == 2 ? lv0 : lv1;
+  store_row_staged8<D>(p, w, h, w.r0 + 32 * wid, ql, hl, st.m, st.l, st.o, stage);
 }
 // ---------------------------------------------------------------------------
 // f32 kernel (v_mfma_f32_32x32x2_f32: exact products, f32 accumulation)
