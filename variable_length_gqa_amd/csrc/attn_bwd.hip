@@ -320,6 +320,48 @@ __device__ __forceinline__ void store_rows_e4m3(void* base, int64_t row_off, int
   }
 }
 
+// The same row block through LDS: the wave writes its 32 x D tile (times
+// mul, 16-bit or E4M3) into `stage` (32 rows of D elements, 16-byte chunks
+// XOR-swizzled by row), reads it back a row chunk per lane and stores whole
+// rows with 16-byte stores: rows first + i * rs (in elements) for i < nrows.
+template <int OUT, int D>
+__device__ __forceinline__ void store_rows_staged(void* base, int64_t first, int64_t rs, int nrows,
+                                                  int ql, int hl, const f32x16 (&acc)[D / 32],
+                                                  float mul, uint8_t* stage) {
+  constexpr int EB = OUT == E_E4M3 ? 1 : 2;  // bytes per element
+  constexpr int ROWB = D * EB, CPR = ROWB / 16;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // elements d = 32 db + 8 g + 4 hl .. +4
+      const float x0 = acc[db][4 * g + 0] * mul, x1 = acc[db][4 * g + 1] * mul;
+      const float x2 = acc[db][4 * g + 2] * mul, x3 = acc[db][4 * g + 3] * mul;
+      if constexpr (OUT == E_E4M3) {
+        const int c = 2 * db + (g >> 1);
+        *reinterpret_cast<uint32_t*>(stage + ql * ROWB + ((c ^ swz8<D>(ql)) * 16) + 8 * (g & 1) +
+                                     4 * hl) =
+            pack4_fp8(sat448(x0), sat448(x1), sat448(x2), sat448(x3));
+      } else {
+        const int c = 4 * db + g;
+        const u32x2 v = {pack2<OUT>(x0, x1), pack2<OUT>(x2, x3)};
+        *reinterpret_cast<u32x2*>(stage + ql * ROWB + ((c ^ swz<D>(ql)) * 16) + 8 * hl) = v;
+      }
+    }
+  }
+  const int lane = ql + 32 * hl;
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int row = RPI * k + lane / CPR, c = lane % CPR;
+    const int pc = OUT == E_E4M3 ? (c ^ swz8<D>(row)) : (c ^ swz<D>(row));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * ROWB + pc * 16);
+    if (row < nrows)
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(base) + (first + row * rs) * EB +
+                                16 * c) = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK and dV
 // ---------------------------------------------------------------------------
@@ -888,13 +930,19 @@ void bwd_dq_kernel(BwdParams p) {
   }
   if (t < t1) tile(t, lk0, lv0, lk1, lv1);
 
-  if (qrow < sb.Lq) {
-    const int64_t row = (int64_t)b * p.q_bs + (int64_t)(sb.q_start + qrow) * p.q_rs +
-                        (int64_t)h * p.q_hs;
+  // every wave has passed the last tile's barrier: the four K/V buffers are
+  // free, one per wave, each at least the size of its dQ tile
+  static_assert(C::TILE >= 32 * 2 * D, "a buffer holds a wave's dQ tile");
+  {
+    uint8_t* stage = wid == 0 ? lk0 : wid == 1 ? lk1 : wid == 2 ? lv0 : lv1;
+    const int r0w = r0 + 32 * wid;
+    const int64_t first = (int64_t)b * p.q_bs + (int64_t)(sb.q_start + r0w) * p.q_rs +
+                          (int64_t)h * p.q_hs;
+    const int nrows = min(32, sb.Lq - r0w);
     if (p.e4m3)
-      store_rows_e4m3<D>(p.dq, row, hl, dq, p.dq_mul);
+      store_rows_staged<E_E4M3, D>(p.dq, first, p.q_rs, nrows, ql, hl, dq, p.dq_mul, stage);
     else
-      store_rows<ELEM, D>(p.dq, row, hl, dq, p.dq_mul);
+      store_rows_staged<ELEM, D>(p.dq, first, p.q_rs, nrows, ql, hl, dq, p.dq_mul, stage);
   }
 }
 
