@@ -304,22 +304,6 @@ __device__ __forceinline__ void store_rows(void* base, int64_t row_off, int hl,
   }
 }
 
-// the same as E4M3 codes (round to nearest even, saturating at +-448)
-template <int D>
-__device__ __forceinline__ void store_rows_e4m3(void* base, int64_t row_off, int hl,
-                                                const f32x16 (&acc)[D / 32], float mul) {
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = db * 32 + g * 8 + 4 * hl;
-      const uint32_t v = pack4_fp8(sat448(acc[db][4 * g + 0] * mul), sat448(acc[db][4 * g + 1] * mul),
-                                   sat448(acc[db][4 * g + 2] * mul), sat448(acc[db][4 * g + 3] * mul));
-      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(base) + row_off + d0) = v;
-    }
-  }
-}
-
 // The same row block through LDS: the wave writes its 32 x D tile (times
 // mul, 16-bit or E4M3) into `stage` (32 rows of D elements, 16-byte chunks
 // XOR-swizzled by row), reads it back a row chunk per lane and stores whole

@@ -548,7 +548,7 @@ void fwd16_kernel(FwdParams p) {
 
   // every wave has passed the last tile's barrier (or the prologue's): the
   // four K/V buffers are free, one per wave, each the size of its O tile
-  static_assert(C::TILE == 32 * 2 * D, "a K/V buffer holds one wave's O tile");
+  static_assert(C::TILE >= 32 * 2 * D, "a K/V buffer holds one wave's O tile");
   uint8_t* stage = wid == 0 ? lk0 : wid == 1 ? lk1 : wid == 2 ? lv0 : lv1;
   store_row_staged<OUT, D>(p, w, h, w.r0 + 32 * wid, ql, hl, st.m, st.l, st.o, stage);
 }
