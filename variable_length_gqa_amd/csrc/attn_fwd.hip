@@ -590,7 +590,7 @@ struct Cfg8 {
 };
 
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 64 ? 4 : 3, D == 64 ? 4 : 3)))
 void fwd8_kernel(FwdParams p) {
   using C = Cfg8<D>;
   using V16 = Cfg5<E_BF16, D, 1>;  // the bf16 V tile layout of the 16-bit kernel
