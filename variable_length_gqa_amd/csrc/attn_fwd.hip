@@ -958,7 +958,9 @@ void fwd32_kernel(FwdParams p) {
 // ---------------------------------------------------------------------------
 
 bool plan_fwd(FwdParams& p, int elem, int head_dim) {
-  // every kernel: one head, 4 waves x 32 query rows per workgroup
+  // every kernel, whatever the element type: one head, 4 waves x 32 query
+  // rows per workgroup
+  (void)elem;
   p.heads_per_wg = 1;
   p.rows_per_wg = 128;
   const int64_t n_qtiles = ((int64_t)p.max_seqlen_q + p.rows_per_wg - 1) / p.rows_per_wg;

@@ -174,7 +174,11 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
 // lds_dst + 16 i .. + 16 (lds_dst is wave-uniform).  The instruction has no
 // register results; it is written out so the compiler does not track it (it
 // cannot tell the LDS buffers apart and would stall every LDS read on it);
-// completion is awaited with an explicit vmcnt wait.
+// completion is awaited with an explicit vmcnt wait.  The LDS address goes in
+// m0, which the compiler reserves and warns about clobbering: no instruction
+// these kernels use reads m0 (gfx950 LDS reads and writes take their address
+// from a VGPR, and there is no indexed register access), so only these
+// statements set and use it.
 __device__ __forceinline__ void dma16(uint32_t lds_dst, uint32_t voff, u32x4 rsrc) {
   const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_dst);
   asm volatile(
