@@ -12,10 +12,14 @@
 //   dq_i  = scale sum_j dS_ij k_j,       dk_j = scale sum_i dS_ij q_i
 // with dk / dv of a kv head summed over its G query heads.
 //
-// Three launches (four with the dK / dV reduction, more for E4M3 inputs):
-//   bwd_rowsum_kernel  delta_i = dO_i.O_i and LSE_i log2(e) per (row, head),
-//                      written head-major into the caller's workspace (so a
-//                      query tile's values are contiguous).
+// Two launches (three with the dK / dV reduction, more for E4M3 inputs):
+//   bwd_dq_kernel      one workgroup per (sequence, 128-row query tile, query
+//                      head), the forward's structure: K/V tiles of 32 keys by
+//                      DMA into LDS, Q^T and dO^T in registers, dQ^T in
+//                      registers.  It first computes the row terms of its rows,
+//                      delta_i = dO_i.O_i and LSE_i log2(e), and writes them
+//                      head-major into the caller's workspace (so a query
+//                      tile's values are contiguous) for the next launch.
 //   bwd_kv_kernel      dK and dV in one pass (E4M3: dV, then dK, two
 //                      launches of one body): one workgroup per (sequence,
 //                      kv head, 128-key tile), 4 waves x 32 keys; K of the
@@ -25,10 +29,6 @@
 //                      and the tile's LSE / delta brought to LDS by DMA (double
 //                      buffered).  dV / dK accumulate in registers: no
 //                      atomics, deterministic.
-//   bwd_dq_kernel      one workgroup per (sequence, 128-row query tile, query
-//                      head), the forward's structure: K/V tiles of 32 keys by
-//                      DMA into LDS, Q^T and dO^T in registers, dQ^T in
-//                      registers.
 // Matrix-core formulation (v_mfma_f32_32x32x16_{bf16,f16}): every product has
 // the operand layouts of the forward kernel.  In dK/dV the lane owns a key:
 //   S  = Q K^T     A = Q rows (LDS), B = K^T (registers)  -> lane: key l % 32,
@@ -84,96 +84,6 @@ __device__ __forceinline__ int64_t ws_index(const BwdParams& p, int b, int64_t r
 }
 __device__ __forceinline__ int64_t ws_plane(const BwdParams& p) {
   return (int64_t)p.d_batch * p.heads * p.d_rows;
-}
-
-// ---------------------------------------------------------------------------
-// delta and the log2-domain LSE
-// ---------------------------------------------------------------------------
-//
-// D/8 lanes per (row, head), 16 bytes of dO and of O each, reduced across
-// those lanes.  Pair order: packed layout (b, r, h) with h fastest, so a wave
-// reads one contiguous stretch of a token's heads; dense layout (b, h, r)
-// with r fastest, which is contiguous in memory and lets the lanes write
-// consecutive floats of the head-major workspace.
-__device__ __forceinline__ void pair_index(const BwdParams& p, int64_t pair, int& b, int& h,
-                                           int64_t& r) {
-  if (p.cu_q) {
-    h = (int)(pair % p.heads);
-    const int64_t rest = pair / p.heads;
-    r = rest % p.d_rows;
-    b = (int)(rest / p.d_rows);
-  } else {
-    r = pair % p.d_rows;
-    const int64_t rest = pair / p.d_rows;
-    h = (int)(rest % p.heads);
-    b = (int)(rest / p.heads);
-  }
-}
-
-template <int ELEM, int D>
-__global__ __launch_bounds__(256) void bwd_rowsum_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;
-  constexpr int PPW = 64 / LPR;
-  const int64_t npairs = (int64_t)p.d_batch * p.d_rows * p.heads;
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * PPW + lane / LPR;
-  const int sub = lane % LPR;
-  float acc = 0.0f;
-  int h = 0, b = 0;
-  int64_t r = 0;
-  if (pair < npairs) {
-    pair_index(p, pair, b, h, r);
-    const int64_t off = (int64_t)b * p.q_bs + r * p.q_rs + (int64_t)h * p.q_hs + sub * 8;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.dout) + off);
-    const u32x4 c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.o) + off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc += lo16<ELEM>(a[i]) * lo16<ELEM>(c[i]) + hi16<ELEM>(a[i]) * hi16<ELEM>(c[i]);
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (pair < npairs && sub == 0) {
-    const float lse = p.lse[(int64_t)b * p.l_bs + r * p.l_rs + (int64_t)h * p.l_hs];
-    const int64_t wi = ws_index(p, b, r, h);
-    p.delta[wi] = lse == -INFINITY ? INFINITY : lse * kLog2e;
-    p.delta[ws_plane(p) + wi] = acc;
-  }
-}
-
-// E4M3 form: D/16 lanes per (row, head), 16 codes of dO and of O each;
-// delta = do_scale o_scale sum(dO8 O8)
-template <int D>
-__global__ __launch_bounds__(256) void bwd_rowsum8_kernel(BwdParams p) {
-  constexpr int LPR = D / 16;
-  constexpr int PPW = 64 / LPR;
-  const int64_t npairs = (int64_t)p.d_batch * p.d_rows * p.heads;
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * PPW + lane / LPR;
-  const int sub = lane % LPR;
-  float acc = 0.0f;
-  int h = 0, b = 0;
-  int64_t r = 0;
-  if (pair < npairs) {
-    pair_index(p, pair, b, h, r);
-    const int64_t off = (int64_t)b * p.q_bs + r * p.q_rs + (int64_t)h * p.q_hs + sub * 16;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.do8) + off);
-    const u32x4 c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.o) + off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        const uint32_t x = fp8x2_to_bf16x2(a[i], hi), y = fp8x2_to_bf16x2(c[i], hi);
-        acc += lo16<E_BF16>(x) * lo16<E_BF16>(y) + hi16<E_BF16>(x) * hi16<E_BF16>(y);
-      }
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (pair < npairs && sub == 0) {
-    const float lse = p.lse[(int64_t)b * p.l_bs + r * p.l_rs + (int64_t)h * p.l_hs];
-    const int64_t wi = ws_index(p, b, r, h);
-    p.delta[wi] = lse == -INFINITY ? INFINITY : lse * kLog2e;
-    p.delta[ws_plane(p) + wi] = acc * p.delta_mul;
-  }
 }
 
 // E4M3 codes -> bf16 copy, 16 codes per thread (n16 = elements / 16)
@@ -779,11 +689,51 @@ void bwd_dq_kernel(BwdParams p) {
       }
     }
   }
+  // The row terms of the lane's row, written to the workspace for the
+  // dK / dV kernel (which runs after this one): delta = dO . O (E4M3: from
+  // the codes, times do_scale o_scale) over the row's two lane halves, and
+  // LSE log2(e) (+inf for a row that sees no key, so its weights are 0).
   float lse2 = INFINITY, dlt = 0.0f;
-  if (qrow < sb.Lq) {
-    const int64_t wi = ws_index(p, p.cu_q ? 0 : b, p.cu_q ? (int64_t)sb.q_start + qrow : qrow, h);
-    lse2 = p.delta[wi];
-    dlt = p.delta[ws_plane(p) + wi];
+  {
+    const int eb = E8 ? 1 : 2;
+    const int64_t ooff = ((int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs +
+                          (int64_t)h * p.q_hs) * eb;
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(reinterpret_cast<const uint8_t*>(p.o) + ooff,
+                                                 sat_bytes((int64_t)sb.Lq * p.q_rs * eb));
+    const uint32_t roff = (uint32_t)qrow * (uint32_t)(p.q_rs * eb);
+    float acc = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < NSB; ++ks) {
+#pragma unroll
+      for (int c = 0; c < (E8 ? 2 : 1); ++c) {
+        const uint32_t o = E8 ? roff + 64 * ks + 32 * hl + 16 * c : roff + (16 * ks + 8 * hl) * 2;
+        const u32x4 ov = bload16(orr, o), dv = of[ks][c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (E8) {
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {
+              const uint32_t x = fp8x2_to_bf16x2(dv[i], hi), y = fp8x2_to_bf16x2(ov[i], hi);
+              acc += lo16<E_BF16>(x) * lo16<E_BF16>(y) + hi16<E_BF16>(x) * hi16<E_BF16>(y);
+            }
+          } else {
+            acc += lo16<ELEM>(dv[i]) * lo16<ELEM>(ov[i]) + hi16<ELEM>(dv[i]) * hi16<ELEM>(ov[i]);
+          }
+        }
+      }
+    }
+    acc = swap_halves_sum(acc);
+    if (qrow < sb.Lq) {
+      const float lse = p.lse[(int64_t)b * p.l_bs + (int64_t)(sb.q_start + qrow) * p.l_rs +
+                              (int64_t)h * p.l_hs];
+      lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+      dlt = E8 ? acc * p.delta_mul : acc;
+      if (hl == 0) {
+        const int64_t wi = ws_index(p, p.cu_q ? 0 : b, p.cu_q ? (int64_t)sb.q_start + qrow : qrow, h);
+        p.delta[wi] = lse2;
+        p.delta[ws_plane(p) + wi] = dlt;
+      }
+    }
   }
 
   // descriptors: 16-bit K and V tiles; E8: the bf16 K copy and the K / V codes
@@ -949,8 +899,7 @@ bool plan_bwd(BwdParams& p, int head_dim) {
   // the Q and dO bytes one dK/dV stream reads, against the 4 MiB L2 of an XCD
   const int64_t stream_bytes = (int64_t)p.max_seqlen_q * (p.group / p.n_split) * head_dim * 2 * 2;
   p.stream_major = stream_bytes >= ((int64_t)4 << 20) ? 1 : 0;
-  const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
-  return pairs / (4 * (64 / (head_dim / 8))) < INT32_MAX / 2;
+  return head_dim > 0;
 }
 
 BwdWorkspace bwd_workspace(int64_t rows, int64_t keys, int64_t heads, int64_t kv_heads,
@@ -975,17 +924,15 @@ void launch_kv(dim3 grid, dim3 blk, hipStream_t stream, const BwdParams& p) {
 }
 
 hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t stream) {
-  const int64_t pairs = (int64_t)p.d_batch * p.d_rows * p.heads;
-  const int ppb = 4 * (64 / (head_dim / (p.e4m3 ? 16 : 8)));
   const int64_t nred = (int64_t)p.kp_rows * p.kv_heads * (head_dim / 8);
   const int64_t streams8 = ((int64_t)p.batch * p.kv_heads * p.n_split + 7) / 8 * 8;
   const int64_t groups8 = ((int64_t)p.n_qtiles * p.batch * p.kv_heads + 7) / 8 * 8;
-  const dim3 g0((unsigned)((pairs + ppb - 1) / ppb)), g1((unsigned)(p.n_ktiles * streams8)),
+  const dim3 g1((unsigned)(p.n_ktiles * streams8)),
       g2((unsigned)(groups8 * p.group)), g3((unsigned)((nred + 255) / 256)), blk(kThreads);
   const bool reduce = p.n_split > 1 || p.e4m3;
   if (p.e4m3) {
-    // bf16 copies of the codes, then the row terms from the codes of dO and O
-    // (V is only an operand of dP, which runs on the codes)
+    // bf16 copies of the codes (V is only an operand of dP, which runs on the
+    // codes)
     const struct { const void* src; void* dst; int64_t n; } w[3] = {
         {p.q8, p.wq, p.n_q}, {p.do8, p.wdo, p.n_q}, {p.k8, p.wk, p.n_k}};
     for (const auto& t : w)
@@ -993,17 +940,12 @@ hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t st
         hipLaunchKernelGGL(widen_e4m3_kernel, dim3((unsigned)((t.n / 16 + 255) / 256)), dim3(256),
                            0, stream, reinterpret_cast<const uint8_t*>(t.src),
                            reinterpret_cast<uint16_t*>(t.dst), t.n / 16);
-    if (pairs > 0) {
-      if (head_dim == 128) hipLaunchKernelGGL((bwd_rowsum8_kernel<128>), g0, blk, 0, stream, p);
-      else hipLaunchKernelGGL((bwd_rowsum8_kernel<64>), g0, blk, 0, stream, p);
-    }
   }
 #define VLGQA_BWD(E, D, E8)                                                    \
   do {                                                                         \
-    if (pairs > 0 && !E8)                                                      \
-      hipLaunchKernelGGL((bwd_rowsum_kernel<E, D>), g0, blk, 0, stream, p);    \
-    if (g1.x > 0) launch_kv<E, D, E8>(g1, blk, stream, p);                    \
+    /* dQ first: it also writes the row terms the dK / dV kernel reads */      \
     if (g2.x > 0) hipLaunchKernelGGL((bwd_dq_kernel<E, D, E8>), g2, blk, 0, stream, p);     \
+    if (g1.x > 0) launch_kv<E, D, E8>(g1, blk, stream, p);                    \
     if (reduce && g3.x > 0)                                                              \
       hipLaunchKernelGGL((bwd_reduce_kernel<E, D>), g3, blk, 0, stream, p);              \
   } while (0)
