@@ -54,6 +54,32 @@ def test_decode_262144_key_cache():
     assert_close("LSE", l.cpu().double().numpy(), L, tl)
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_bwd_unsplit_heads_many_short_sequences(head_dim):
+    """400 sequences of 0-96 tokens, 8 kv heads of 2 query heads: a grid of
+    well over two key-tile workgroups per CU whose loops are all short, so the
+    dK / dV workgroups cover the whole head group and store dK and dV directly
+    (no partial sums to reduce).  Backward against the oracle on every
+    element."""
+    g = torch.Generator().manual_seed(707 + head_dim)
+    lengths = [int(n) for n in torch.randint(0, 97, (400,), generator=g)]
+    H, Hkv, D = 16, 8, head_dim
+    x = W.make_varlen(lengths, num_heads=H, num_kv_heads=Hkv, head_dim=D, dtype=torch.bfloat16,
+                      causal=True, seed=708 + head_dim)
+    xd = x.to(DEV)
+    B, mx = len(lengths), max(lengths)
+    o, l = vg.varlen_attention_fwd(xd.q, xd.k, xd.v, xd.cu_q, xd.cu_k, B, H, Hkv, mx, mx, D, True)
+    dO = W.make_dout(x.q, 709)
+    dq, dk, dv = vg.varlen_attention_bwd(dO.to(DEV), xd.q, xd.k, xd.v, o, l, xd.cu_q, xd.cu_k, B,
+                                         H, Hkv, mx, mx, D, True)
+    torch.cuda.synchronize()
+    refs = oracle.varlen_attention_bwd(dO, x.q, x.k, x.v, x.cu_q, x.cu_k, H, Hkv, True,
+                                       workers=oracle_workers())
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        err = float(np.abs(to_f64(got.cpu()) - ref).max())
+        assert err <= 1.5e-2 * float(np.abs(ref).max()), (name, err)
+
+
 def test_many_tiny_sequences_forward_and_backward():
     """500 sequences of 0-40 tokens (many empty or shorter than one tile) and
     a group of 16 query heads per kv head: forward and backward against the

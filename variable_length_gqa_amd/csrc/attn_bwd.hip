@@ -888,10 +888,19 @@ bool plan_bwd(BwdParams& p, int head_dim) {
   const int64_t nk = ((int64_t)p.max_seqlen_k + kTileB - 1) / kTileB;
   const int64_t nq = ((int64_t)p.max_seqlen_q + kTileB - 1) / kTileB;
   // Two workgroups per (kv head, key tile), each over half of the group's
-  // query heads, when the group has an even size: the first key tiles of a
-  // causal sequence carry the most work, and halving their loop brings the
-  // longest workgroup down to about the average load of a CU slot.
-  p.n_split = (p.group % 2 == 0 && p.part != nullptr) ? 2 : 1;
+  // query heads (the group must have an even size), when one workgroup's loop
+  // would be long or the grid small.  Under a causal mask or a window the
+  // first key tiles carry the most work: ceil(max_seqlen_q / 32) * group
+  // stages for the longest sequence (fewer under a window); past 256 stages,
+  // halving that loop brings the longest workgroup down to about the average
+  // load of a CU slot.  A grid of fewer than two workgroups per CU (256 CUs)
+  // is split for parallelism.  Otherwise the split costs more than it gains:
+  // its reduction pass reads and writes f32 partials of dK and dV.
+  const int64_t wg1 = ((int64_t)p.kp_rows + kTileB - 1) / kTileB * p.kv_heads;
+  int64_t seen = p.max_seqlen_q;
+  if (p.window > 0 && (int64_t)p.window + kTileB < seen) seen = (int64_t)p.window + kTileB;
+  const bool long_loop = (p.causal || p.window > 0) && (seen + 31) / 32 * p.group > 256;
+  p.n_split = (p.group % 2 == 0 && p.part != nullptr && (wg1 < 512 || long_loop)) ? 2 : 1;
   if (nk * ((int64_t)p.batch * p.kv_heads * p.n_split + 8) > INT32_MAX / 2) return false;
   if ((nq * p.batch * p.kv_heads + 8) * p.group > INT32_MAX / 2) return false;
   p.n_ktiles = (int32_t)nk;
