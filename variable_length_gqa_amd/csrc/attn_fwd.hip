@@ -54,7 +54,10 @@ constexpr float kPartialSumBound = 32768.0f;
 // its G query heads (heads_per_wg at a time) and read the same K/V, so they
 // are placed on consecutive slots of ONE XCD and share its L2.  Groups are
 // ordered by descending query tile: under a causal mask later tiles see more
-// keys, so the longest work is dispatched first.
+// keys, so the longest work is dispatched first.  Under a sliding window the
+// tiles of one sequence come together instead (sequence-major, descending
+// within it): nearby tiles read nearly the same window of K/V, and the
+// windows of the sequences interleaved would not fit an XCD's L2 together.
 struct Work {
   int b, kvh, h0, r0;
   int q_start, Lq, k_start, Lk;
@@ -71,8 +74,14 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, Work& w) {
   if (grp >= p.n_groups) return false;
   w.kvh = grp % p.kv_heads;
   const int t2 = grp / p.kv_heads;
-  w.b = t2 % p.batch;
-  const int tidx = t2 / p.batch;
+  int tidx;
+  if (p.window > 0) {  // a sequence's tiles together: they share their K/V windows
+    w.b = t2 / p.n_qtiles;
+    tidx = t2 % p.n_qtiles;
+  } else {
+    w.b = t2 % p.batch;
+    tidx = t2 / p.batch;
+  }
   w.r0 = (p.n_qtiles - 1 - tidx) * p.rows_per_wg;
   w.h0 = w.kvh * p.group + g2 * p.heads_per_wg;
   w.q_start = 0;
