@@ -71,7 +71,11 @@ enum vlgqa_dtype { VLGQA_F32 = 0, VLGQA_F16 = 1, VLGQA_BF16 = 2 };
  *                cu[batch_size] = total_q.  Likewise cu_seqlens_k for k/v.
  *                The contents are trusted (they are device memory).
  *   max_seqlen_q / max_seqlen_k  upper bounds of the per-sequence lengths
- *                (they size the launch; a longer sequence is only partly computed).
+ *                (they size the launch).  EINVAL when total_q > batch_size *
+ *                max_seqlen_q (or likewise for k): some sequence must be longer.
+ *                A sequence longer than max_seqlen_q that this test cannot see
+ *                gets its rows beyond ceil(max_seqlen_q / 128) * 128 written as
+ *                NaN (O and LSE), never left unwritten.
  *   causal       0/1.  There is no window on this entry point.
  *   out          [total_q, num_heads, head_dim]      dtype
  *   lse          [total_q, num_heads]                float32, natural log
@@ -210,7 +214,10 @@ int flash_attention_fwd_fp8(const void* q, const void* k, const void* v,
  *   dout, out, q, dq  [total_q, num_heads, head_dim]      dtype
  *   k, v, dk, dv      [total_k, num_kv_heads, head_dim]   dtype
  *   lse               [total_q, num_heads]                float32
- *   cu_seqlens_q/k, max_seqlen_q/k, causal: as in varlen_attention_fwd.
+ *   cu_seqlens_q/k, max_seqlen_q/k, causal: as in varlen_attention_fwd
+ *   (the same EINVAL when total_q / total_k exceed batch_size times the bound;
+ *   a sequence longer than its bound that the check cannot see leaves its
+ *   gradient rows beyond the bound unwritten: a broken caller promise).
  *
  * Errors: as varlen_attention_fwd, plus EUNSUPPORTED for a dtype other than
  * VLGQA_BF16 / VLGQA_F16.

@@ -10,19 +10,22 @@ import torch
 
 # tolerances against the f64 oracle (max absolute error)
 #   f32 storage: O and LSE 1e-4; bf16: O 1e-2, LSE 1e-3 (the stated bounds).
-#   A 16-bit O is compared with the allowance tol + half an ulp of the output
-#   dtype at |O| (see assert_close): the stated bound limits the computation,
-#   not the final rounding to storage, which alone reaches 7.8e-3 at |O| in
-#   [2, 4) and 1.6e-2 at [4, 8) in bf16 -- even the exact O stored in bf16
-#   would fail a flat 1e-2 there.
-#   f16: O 4e-3, LSE 1e-3 -- derived: P is rounded to f16 (relative 2^-11) before
-#   P.V, so 4e-3 covers it with margin; scores are exact products accumulated
-#   in f32, so LSE errors stay near 1e-5.
+#   The O bound limits the computation; a 16-bit O is also allowed the final
+#   rounding to its storage dtype, half an ulp at |O| (see assert_close), which
+#   alone reaches 7.8e-3 at |O| in [2, 4) and 1.6e-2 at [4, 8) in bf16 -- even
+#   the exact O stored in bf16 would fail a flat 1e-2 there.  Per binade
+#   [2^e, 2^(e+1)) of |O| the allowance is therefore tol + 2^(e-8) (bf16) and
+#   tol + 2^(e-11) (f16).
+#   f16: O 3e-3 for the computation alone -- derived: P is rounded to f16
+#   (relative error <= 2^-11) before P.V, so O moves by at most
+#   2^-11 * max|v| <= 2.9e-3 for |v| <= 6 (every f16 case draws N(0,1) values);
+#   the f32 products and sums add ~1e-6.  Scores are exact products summed in
+#   f32, so LSE errors stay near 1e-5 (bound 1e-3).
 #   E4M3: |o8 * o_scale - O| <= 6e-2 * amax|O| and LSE 1e-3.
 TOL = {
     torch.float32: (1e-4, 1e-4),
     torch.bfloat16: (1e-2, 1e-3),
-    torch.float16: (4e-3, 1e-3),
+    torch.float16: (3e-3, 1e-3),
 }
 FP8_REL_TOL = 6e-2
 FP8_LSE_TOL = 1e-3
@@ -50,36 +53,39 @@ def half_ulp(x: np.ndarray, dtype) -> np.ndarray:
     """Half the spacing of ``dtype`` (bf16 / f16) at |x|: the largest error of
     rounding x to that dtype (normal range)."""
     _, e = np.frexp(np.abs(x))               # |x| = m 2^e, m in [0.5, 1)
-    return np.ldexp(1.0, e - 2 - MANT_BITS[dtype])
+    return np.where(x == 0, 0.0, np.ldexp(1.0, e - 2 - MANT_BITS[dtype]))  # 0 is stored exactly
 
 
 def assert_close(name, got, ref, tol, dtype=None):
-    """Max-abs comparison; -inf entries must coincide exactly.  With a 16-bit
-    ``dtype`` (the storage of ``got``) each element may also differ by half an
-    ulp of that dtype at the reference value."""
+    """Max-abs comparison.  Shapes must match, the result must hold no NaN and
+    its -inf entries must coincide with the reference's.  With a 16-bit
+    ``dtype`` (the storage of ``got``) each finite element may differ by ``tol``
+    plus half an ulp of that dtype at the reference value (the rounding of the
+    result to storage).  Returns the raw max |err| over the finite entries."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    if dtype in MANT_BITS:
-        f0 = np.isfinite(ref)
-        excess = np.where(f0, np.abs(got - np.where(f0, ref, 0)) - half_ulp(np.where(f0, ref, 0), dtype), 0)
-        worst = float(excess.max()) if excess.size else 0.0
-        assert not np.isnan(got).any(), f"{name}: NaN in the result"
-        assert worst <= tol, f"{name}: max |err| - half ulp {worst:.3e} > {tol:.1e} at " \
-            f"{np.unravel_index(int(np.argmax(excess)), got.shape)}"
-        return worst
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert not np.isnan(got).any(), f"{name}: NaN in the result"
     ninf_ref, ninf_got = np.isneginf(ref), np.isneginf(got)
     assert (ninf_ref == ninf_got).all(), f"{name}: -inf pattern differs " \
         f"({int(ninf_ref.sum())} expected, {int(ninf_got.sum())} got)"
     f = ~ninf_ref
-    if f.any():
-        err = np.abs(got[f] - ref[f])
-        worst = float(err.max())
-        assert worst <= tol, f"{name}: max |err| {worst:.3e} > {tol:.1e} " \
-            f"at {np.unravel_index(int(np.argmax(np.where(f, np.abs(got - np.where(f, ref, 0)), -1))), got.shape)}"
-        return worst
-    return 0.0
+    if not f.any():
+        return 0.0
+    r0 = np.where(f, ref, 0.0)
+    err = np.where(f, np.abs(got - r0), 0.0)
+    raw = float(err.max())
+    allow = np.full(ref.shape, float(tol))
+    if dtype in MANT_BITS:
+        allow = allow + half_ulp(r0, dtype)
+    excess = err - allow
+    worst = int(np.argmax(excess))
+    at = np.unravel_index(worst, got.shape)
+    assert excess.flat[worst] <= 0.0, \
+        f"{name}: |err| {err.flat[worst]:.3e} > allowed {allow.flat[worst]:.3e} at {at} " \
+        f"(ref {ref.flat[worst]:.6g}, got {got.flat[worst]:.6g}; raw max |err| {raw:.3e}, " \
+        f"tol {tol:.1e}{' + half an ulp' if dtype in MANT_BITS else ''})"
+    return raw
 
 
 def e4m3_decode_torch(codes: torch.Tensor) -> np.ndarray:

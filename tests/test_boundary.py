@@ -105,8 +105,21 @@ def test_varlen_rejects(lib, kw, code, arg):
 def test_varlen_empty_problems_return_ok_without_pointers(lib):
     assert varlen(lib, b=0, q=0, k=0, v=0, cq=0, ck=0, out=0, lse=0) == _lib.VLGQA_OK
     assert varlen(lib, tq=0, q=0, k=0, v=0, cq=0, ck=0, out=0, lse=0) == _lib.VLGQA_OK
-    assert varlen(lib, mq=0, q=0, k=0, v=0, cq=0, ck=0, out=0, lse=0) == _lib.VLGQA_OK
+    assert varlen(lib, tq=0, mq=0, q=0, k=0, v=0, cq=0, ck=0, out=0, lse=0) == _lib.VLGQA_OK
     assert err(lib) == ""
+
+
+@pytest.mark.parametrize("kw,arg", [
+    (dict(mq=0), "max_seqlen_q"),            # tokens but no room for any
+    (dict(mq=313), "max_seqlen_q"),          # 3 * 313 < 940: some sequence is longer
+    (dict(mk=300), "max_seqlen_k"),
+])
+def test_varlen_rejects_max_seqlen_below_the_average(lib, kw, arg):
+    assert varlen(lib, **kw) == EINVAL
+    assert err(lib).startswith(arg + ":"), err(lib)
+    if arg == "max_seqlen_q":
+        assert varlen_bwd(lib, **kw) == EINVAL
+        assert err(lib).startswith(arg + ":"), err(lib)
 
 
 @pytest.mark.parametrize("kw,code,arg", [
@@ -358,9 +371,9 @@ def test_sequences_past_32bit_buffer_offsets_are_rejected(lib):
     # one sequence's rows must span less than 4 GiB (the kernels' buffer
     # descriptors use 32-bit byte offsets): 300000 tokens x 64 heads x 128 x 2 B
     assert varlen(lib, h=64, hkv=8, d=128, dtype=BF16, mq=300000, mk=512, tq=300000,
-                  tk=300000) == EINVAL
+                  tk=940) == EINVAL
     assert err(lib).startswith("max_seqlen_q:"), err(lib)
-    assert varlen(lib, h=64, hkv=64, d=128, dtype=BF16, mq=512, mk=300000, tq=300000,
+    assert varlen(lib, h=64, hkv=64, d=128, dtype=BF16, mq=512, mk=300000, tq=940,
                   tk=300000) == EINVAL
     assert err(lib).startswith("max_seqlen_k:"), err(lib)
     assert dense(lib, b=1, sq=1 << 24, cap=1 << 24, n=1 << 24) == EINVAL

@@ -111,6 +111,25 @@ def test_varlen_only_valid_rows_written():
     assert_close("LSE", l[:T].double().numpy(), L, 1e-3)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=str)
+def test_varlen_rows_beyond_max_seqlen_are_nan(dtype):
+    """A sequence longer than max_seqlen_q (300 > 200, which the host's
+    total_q <= batch_size * max_seqlen_q test cannot see) gets its rows past the
+    launch's reach (256 = two 128-row tiles) written as NaN, never left stale;
+    the rows within reach and the other sequence are still exact."""
+    x = W.make_varlen([300, 10], num_heads=4, num_kv_heads=2, head_dim=128, dtype=dtype,
+                      causal=True, seed=160)
+    out = torch.zeros((310, 4, 128), dtype=dtype, device=DEV)
+    lse = torch.zeros((310, 4), dtype=torch.float32, device=DEV)
+    o, l = run_varlen(x, out=out, lse=lse, max_q=200)
+    assert torch.isnan(o[256:300].float()).all() and torch.isnan(l[256:300]).all()
+    O, L = oracle.varlen_attention_fwd(x.q, x.k, x.v, x.cu_q, x.cu_k, 4, 2, True)
+    keep = np.r_[0:256, 300:310]
+    to, tl = TOL[dtype]
+    assert_close("O", to_f64(o)[keep], O[keep], to, dtype)
+    assert_close("LSE", l.double().numpy()[keep], L[keep], tl)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=str)
 def test_causal_first_row_is_v0_bit_exact(dtype):
     x = W.make_varlen([300, 1, 129], num_heads=8, num_kv_heads=2, head_dim=128, dtype=dtype,
@@ -228,3 +247,58 @@ def test_fp8_row0_reproduces_v_codes():
     torch.cuda.synchronize()
     for h in range(4):
         assert torch.equal(out[0, h, 0].cpu(), d.v[0, 0, 0])
+
+
+def _fp8_case(B, H, Hkv, Sq, Sk, D, causal, seed):
+    """E4M3 q [B,H,Sq,D] and k, v [B,Hkv,Sk,D] from seeded N(0,1) draws, per-tensor
+    scales amax/448."""
+    g = torch.Generator().manual_seed(seed)
+    q8, qs = W.quantize_e4m3(torch.randn(B, H, Sq, D, generator=g))
+    k8, ks = W.quantize_e4m3(torch.randn(B, Hkv, Sk, D, generator=g))
+    v8, vs = W.quantize_e4m3(torch.randn(B, Hkv, Sk, D, generator=g))
+    return W.Dense(q8, k8, v8, H, Hkv, D, causal, 0, None, f"fp8 {Sq} q x {Sk} k",
+                   {"q_scale": qs, "k_scale": ks, "v_scale": vs})
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Sk,D", [(200, 333, 128), (333, 200, 128), (300, 517, 64),
+                                     (1, 300, 128)], ids=str)
+def test_fp8_unequal_query_and_key_lengths(Sq, Sk, D, causal):
+    # causal with Sq > Sk: the first Sq - Sk rows see no key (O = 0, LSE = -inf)
+    d = _fp8_case(2, 8, 2, Sq, Sk, D, causal, 140 + Sq + D)
+    out = check_fp8(d)
+    if causal and Sq > Sk:
+        assert (out[:, :, :Sq - Sk].cpu() == 0).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_output_saturates(causal):
+    """o_scale a quarter of amax|O|/448: the outputs beyond the E4M3 range must
+    be stored as the saturated +-448 codes (0x7E / 0xFE, the oracle's), never
+    as a NaN code; every output is within 6e-2 of the representable range of
+    the oracle's value clipped to that range."""
+    d = _fp8_case(2, 8, 2, 300, 300, 128, causal, 150)
+    s = d.scales
+    _, _, O1 = oracle.flash_attention_fwd_fp8(d.q, d.k, d.v, 8, 2, causal, s["q_scale"],
+                                              s["k_scale"], s["v_scale"], 1.0)
+    o_scale = float(np.abs(O1).max()) / 448.0 / 4.0
+    o8, L, O = oracle.flash_attention_fwd_fp8(d.q, d.k, d.v, 8, 2, causal, s["q_scale"],
+                                              s["k_scale"], s["v_scale"], o_scale)
+    dd = d.to(DEV)
+    out, lse = vg.flash_attention_fwd_fp8(dd.q, dd.k, dd.v, 8, 2, 128, causal, s["q_scale"],
+                                          s["k_scale"], s["v_scale"], o_scale)
+    torch.cuda.synchronize()
+    codes = out.cpu().numpy()
+    assert not ((codes & 0x7F) == 0x7F).any(), "NaN code in the output"
+    x = O / o_scale
+    sure = np.abs(x) >= 480.0           # saturated whatever the computation's rounding
+    assert int(sure.sum()) > 100, int(sure.sum())
+    np.testing.assert_array_equal(codes[sure], o8[sure])
+    assert set(np.unique(o8[sure]).tolist()) <= {0x7E, 0xFE}
+    top = 448.0 * o_scale
+    got = e4m3_decode_torch(out.cpu()) * o_scale
+    err = np.abs(got - np.clip(O, -top, top))
+    print(f"saturated {int(sure.sum())} of {x.size}; max err {err.max() / top:.3e} of 448 o_scale")
+    assert err.max() <= FP8_REL_TOL * top, err.max() / top
+    assert float((codes == o8).mean()) > 0.9
+    assert_close("LSE", lse.cpu().double().numpy(), L, FP8_LSE_TOL)

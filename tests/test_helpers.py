@@ -32,3 +32,42 @@ def test_assert_close_allows_storage_rounding_only():
         pass
     else:
         raise AssertionError("a wrong code passed")
+
+
+def test_assert_close_checks_shape_and_infinities_on_every_path():
+    ref = np.array([[0.5, -np.inf], [1.0, 2.0]])
+    got = ref.copy()
+    for dt in (None, torch.bfloat16, torch.float16):
+        assert assert_close("x", got, ref, 1e-3, dt) == 0.0
+        for bad in (got[:1], got.reshape(4)):                  # broadcastable or reshaped
+            try:
+                assert_close("x", bad, ref, 1e-3, dt)
+            except AssertionError:
+                pass
+            else:
+                raise AssertionError(f"a shape mismatch passed ({dt})")
+        fin = got.copy()
+        fin[0, 1] = -1e30                                      # finite where -inf is expected
+        try:
+            assert_close("x", fin, ref, 1e-3, dt)
+        except AssertionError:
+            pass
+        else:
+            raise AssertionError(f"a finite value in place of -inf passed ({dt})")
+
+
+def test_assert_close_returns_the_raw_error():
+    ref = np.array([0.25, 3.0])
+    got = np.array([0.25, 3.0 + 0.01])
+    assert abs(assert_close("x", got, ref, 1e-2, torch.bfloat16) - 0.01) < 1e-15
+    assert abs(assert_close("x", got, ref, 2e-2) - 0.01) < 1e-15
+
+
+def test_zero_is_allowed_no_rounding():
+    # a reference of exactly 0 is stored exactly: only tol is allowed there
+    try:
+        assert_close("x", np.array([1.5e-3]), np.array([0.0]), 1e-3, torch.bfloat16)
+    except AssertionError:
+        pass
+    else:
+        raise AssertionError("half an ulp was allowed at 0")

@@ -267,6 +267,72 @@ def test_sampled_rows_match_full():
         assert abs(Ls[n] - L[t, h]) < 1e-13
 
 
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 3)])
+def test_dense_rows_equal_brute_force(causal, window):
+    """dense_rows on a GQA group of 3 (a strided head map would differ), with
+    a K/V capacity of 12 attended to kv_seq_len = 9 (the tail is NaN, so any
+    read of it poisons the row) and Sq = 7 != 9 (swapped extents would move the
+    causal diagonal): every sampled row equals the pure-Python brute force."""
+    g = torch.Generator().manual_seed(31)
+    B, H, Hkv, Sq, cap, n, D = 2, 6, 2, 7, 12, 9, 4
+    q = torch.randn(B, H, Sq, D, generator=g, dtype=torch.float64)
+    k = torch.randn(B, Hkv, cap, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, Hkv, cap, D, generator=g, dtype=torch.float64)
+    k[:, :, n:] = math.nan
+    v[:, :, n:] = math.nan
+    samples = [(0, 0, 0), (0, 1, 6), (0, 2, 3), (1, 3, 1), (1, 4, 5), (1, 5, 6), (0, 5, 2)]
+    Os, Ls = oracle.dense_rows(q, k, v, H, Hkv, causal, samples, window=window, kv_seq_len=n)
+    assert Os.shape == (len(samples), D) and Ls.shape == (len(samples),)
+    for r, (b, h, i) in enumerate(samples):
+        kvh = h // (H // Hkv)
+        keys = k[b, kvh, :n].tolist()
+        vals = v[b, kvh, :n].tolist()
+        ob, lb = brute.attention_one_row(q[b, h, i].tolist(), keys, vals,
+                                         brute.visible_keys(i, Sq, n, causal, window),
+                                         1 / math.sqrt(D))
+        np.testing.assert_allclose(Os[r], ob, rtol=0, atol=1e-12)
+        assert abs(Ls[r] - lb) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_rows_equal_brute_force_and_saturate(causal):
+    """fp8_rows against the brute force on inputs decoded by torch's own float8
+    type (not the oracle codec): Sq = 5 queries on Sk = 8 keys, a GQA group of
+    2; o_scale is a third of amax|O|/448, so some codes saturate.  The codes are
+    torch's round-to-nearest-even cast where |O/o_scale| <= 448 and the
+    saturated +-448 (0x7E / 0xFE) beyond."""
+    g = torch.Generator().manual_seed(32)
+    B, H, Hkv, Sq, Sk, D = 2, 4, 2, 5, 8, 8
+    q8, qs = W.quantize_e4m3(torch.randn(B, H, Sq, D, generator=g))
+    k8, ks = W.quantize_e4m3(torch.randn(B, Hkv, Sk, D, generator=g))
+    v8, vs = W.quantize_e4m3(torch.randn(B, Hkv, Sk, D, generator=g))
+    dec = lambda c, s: (c.view(torch.float8_e4m3fn).to(torch.float64) * s)
+    qf, kf, vf = dec(q8, qs), dec(k8, ks), dec(v8, vs)
+    samples = [(b, h, i) for b in range(B) for h in range(H) for i in range(Sq)]
+    ref = []
+    for (b, h, i) in samples:
+        kvh = h // (H // Hkv)
+        ob, lb = brute.attention_one_row(qf[b, h, i].tolist(), kf[b, kvh].tolist(),
+                                         vf[b, kvh].tolist(),
+                                         brute.visible_keys(i, Sq, Sk, causal, 0),
+                                         1 / math.sqrt(D))
+        ref.append((ob, lb))
+    Ob = np.array([o for o, _ in ref])
+    Lb = np.array([l for _, l in ref])
+    o_scale = float(np.abs(Ob).max()) / 448.0 / 3.0
+    codes, O, L = oracle.fp8_rows(q8, k8, v8, H, Hkv, causal, samples, qs, ks, vs, o_scale)
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    fin = np.isfinite(Lb)
+    assert (np.isfinite(L) == fin).all()
+    np.testing.assert_allclose(L[fin], Lb[fin], rtol=0, atol=1e-12)
+    x = Ob / o_scale
+    big = np.abs(x) > 448.0
+    assert big.any() and (~big).any()
+    want = torch.from_numpy(np.where(big, 0.0, x)).to(torch.float8_e4m3fn).view(torch.uint8)
+    want = np.where(big, np.where(x > 0, 0x7E, 0xFE), want.numpy())
+    np.testing.assert_array_equal(codes, want)
+
+
 def test_worker_pool_gives_same_result():
     x = W.make_varlen([20, 31, 9], num_heads=4, num_kv_heads=2, head_dim=8,
                       dtype=torch.float32, seed=24)

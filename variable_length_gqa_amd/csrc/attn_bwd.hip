@@ -52,6 +52,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "bwd_params.h"
 #include "kernel_common.h"
 
@@ -148,12 +150,12 @@ __device__ __forceinline__ void tile_dma_offsets(uint32_t (&voff)[T16<D>::CPT], 
 }
 
 template <int D>
-__device__ __forceinline__ void dma_tile16(const uint8_t* buf, u32x4 rsrc, uint32_t base, int wid,
+__device__ __forceinline__ void dma_tile16(const uint8_t* buf, __amdgpu_buffer_rsrc_t rsrc,
+                                           uint32_t base, int wid,
                                            const uint32_t (&voff)[T16<D>::CPT]) {
   using C = T16<D>;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)buf;
 #pragma unroll
-  for (int n = 0; n < C::CPT; ++n) dma16(lds0 + (wid * C::CPT + n) * 1024, base + voff[n], rsrc);
+  for (int n = 0; n < C::CPT; ++n) dma16(buf + (wid * C::CPT + n) * 1024, base + voff[n], rsrc);
 }
 
 // row-operand read offset of lane (row ql, half hl) for k-step 0: the
@@ -289,9 +291,18 @@ void bwd_kv_kernel(BwdParams p) {
   constexpr int OFF_T = !E8 ? (MODE == MODE_DV ? C::TILE : 0) : (MODE == MODE_DV ? T8 : 2 * T8);
   constexpr int OFF_W = !E8 ? 2 * C::TILE : (MODE == MODE_DV ? T8 + C::TILE : 2 * T8 + C::TILE);
   constexpr int STAGE = OFF_W + 256;
-  // fused: V rows of the workgroup's keys after the two stages (4 tiles)
-  constexpr int OFF_V = 2 * STAGE;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE + (FUSED ? 4 * C::TILE : 0)];
+  // fused: V rows of the workgroup's keys (4 tiles) in an array of their own
+  // The two stage buffers and the V tiles are arrays of their own and the
+  // stage loop is unrolled by two, so every DMA and every read names its
+  // buffer at compile time: the compiler holds a read back only for the DMA
+  // into that same buffer, not for the next stage's DMA into the other one.
+  __shared__ __attribute__((aligned(1024))) uint8_t lst0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lst1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lvk[FUSED ? 4 * C::TILE : 16];
+  auto stage_buf = [&](auto U) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(U)::value == 0) return lst0;
+    else return lst1;
+  };
 
   // work: a "stream" is (batch, kv head, split) -- the query heads whose Q /
   // dO it reads; one split covers group / n_split query heads.  Blocks go to
@@ -353,10 +364,10 @@ void bwd_kv_kernel(BwdParams p) {
       // sequence arrive as zeros); awaited with the first stage
       uint32_t voffk[C::CPT];
       tile_dma_offsets<D>(voffk, wid, lane, (uint32_t)(p.k_rs * 2));
-      const u32x4 vrw = rsrc_words(vbase + koff, bytes);
+      const __amdgpu_buffer_rsrc_t vrw = make_rsrc(vbase + koff, bytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        dma_tile16<D>(lds + OFF_V + i * C::TILE, vrw, (uint32_t)(k0 + 32 * i) * (uint32_t)(p.k_rs * 2),
+        dma_tile16<D>(lvk + i * C::TILE, vrw, (uint32_t)(k0 + 32 * i) * (uint32_t)(p.k_rs * 2),
                       wid, voffk);
     }
   }
@@ -393,28 +404,30 @@ void bwd_kv_kernel(BwdParams p) {
   const int64_t plane = ws_plane(p);
 
   // DMA of stage s into buffer u: the tiles of (head, tile) and its lse2/delta
-  auto issue = [&](int s, int u) __attribute__((always_inline)) {
+  auto issue = [&](int s, auto U) __attribute__((always_inline)) {
     const int hh = s % gsplit, t = tb - 1 - s / gsplit;
     const int h = hbase + hh;
     const int64_t qrow0 = (int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs + (int64_t)h * p.q_hs;
     const uint32_t bytes = sat_bytes((int64_t)sb.Lq * p.q_rs * 2);
     const uint32_t base = (uint32_t)(t * 32) * (uint32_t)(p.q_rs * 2);
-    const uint8_t* buf = lds + u * STAGE;
-    const u32x4 q16 = rsrc_words(reinterpret_cast<const uint8_t*>(p.q) + qrow0 * 2, bytes);
-    const u32x4 d16 = rsrc_words(reinterpret_cast<const uint8_t*>(p.dout) + qrow0 * 2, bytes);
+    const uint8_t* buf = stage_buf(U);
+    const __amdgpu_buffer_rsrc_t q16 = make_rsrc(reinterpret_cast<const uint8_t*>(p.q) + qrow0 * 2,
+                                                 bytes);
+    const __amdgpu_buffer_rsrc_t d16 = make_rsrc(
+        reinterpret_cast<const uint8_t*>(p.dout) + qrow0 * 2, bytes);
     if constexpr (!E8) {
       dma_tile16<D>(buf, q16, base, wid, voff);
       dma_tile16<D>(buf + C::TILE, d16, base, wid, voff);
     } else {
       const uint32_t bytes8 = sat_bytes((int64_t)sb.Lq * p.q_rs);
       const uint32_t base8 = (uint32_t)(t * 32) * (uint32_t)p.q_rs;
-      const uint32_t l8 = (uint32_t)(uintptr_t)(lds_void*)buf + wid * 1024;
+      const uint8_t* l8 = buf + wid * 1024;
       if (has8) {
         dma16(l8 + OFF_S, base8 + voff8,
-              rsrc_words(reinterpret_cast<const uint8_t*>(p.q8) + qrow0, bytes8));
+              make_rsrc(reinterpret_cast<const uint8_t*>(p.q8) + qrow0, bytes8));
         if constexpr (MODE == MODE_DK)
           dma16(l8 + OFF_DP, base8 + voff8,
-                rsrc_words(reinterpret_cast<const uint8_t*>(p.do8) + qrow0, bytes8));
+                make_rsrc(reinterpret_cast<const uint8_t*>(p.do8) + qrow0, bytes8));
       }
       dma_tile16<D>(buf + OFF_T, MODE == MODE_DV ? d16 : q16, base, wid, voff);
     }
@@ -423,29 +436,31 @@ void bwd_kv_kernel(BwdParams p) {
       // the sequence arrive as zeros
       const int64_t wi = ws_index(p, p.cu_q ? 0 : b, p.cu_q ? (int64_t)sb.q_start : 0, h);
       const float* src = p.delta + wi + (wid == 1 ? plane : 0);
-      dma16((uint32_t)(uintptr_t)(lds_void*)(buf + OFF_W + wid * 128),
-            (uint32_t)(t * 32 * 4 + lane * 16), rsrc_words(src, sat_bytes((int64_t)sb.Lq * 4)));
+      dma16(buf + OFF_W + wid * 128, (uint32_t)(t * 32 * 4 + lane * 16),
+            make_rsrc(src, sat_bytes((int64_t)sb.Lq * 4)));
     }
   };
 
-  if (nst > 0) issue(0, 0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (nst > 0) issue(0, S0{});
   wait_vm_all();
   lds_barrier();
 
-  for (int s = 0; s < nst; ++s) {
-    const int u = s & 1;
-    if (s + 1 < nst) issue(s + 1, u ^ 1);
+  // stage s sits in buffer s % 2
+  auto stage = [&](int s, auto U) __attribute__((always_inline)) {
+    if (s + 1 < nst) issue(s + 1, std::integral_constant<int, 1 - decltype(U)::value>{});
     const int t = tb - 1 - s / gsplit;
     const int q0 = t * 32;
     if (wave_keys && q0 < wqb && q0 + 32 > wqa) {
-      const uint8_t* sbuf = lds + u * STAGE;
+      const uint8_t* sbuf = stage_buf(U);
       const uint8_t* st_ = sbuf + OFF_S;    // A operand of S (Q rows)
       const uint8_t* dpt = sbuf + OFF_DP;   // A operand of dP (dO rows)
       const float* wsv = reinterpret_cast<const float*>(sbuf + OFF_W);
       f32x16 sc = {}, dp = {};
       if constexpr (FUSED) {
         // B operand of dP: V^T of the wave's keys, the same row reads as Q
-        const uint8_t* vk = lds + OFF_V + wid * C::TILE;
+        const uint8_t* vk = lvk + wid * C::TILE;
 #pragma unroll
         for (int ks = 0; ks < C::NS; ++ks) {
           const uint32_t ro = roff0 ^ (uint32_t)(ks << 5);
@@ -537,6 +552,10 @@ void bwd_kv_kernel(BwdParams p) {
     }
     wait_vm_all();
     lds_barrier();
+  };
+  for (int s = 0; s < nst; s += 2) {
+    stage(s, S0{});
+    if (s + 1 < nst) stage(s + 1, S1{});
   }
 
   if (key < sb.Lk) {
@@ -737,19 +756,20 @@ void bwd_dq_kernel(BwdParams p) {
   }
 
   // descriptors: 16-bit K and V tiles; E8: the bf16 K copy and the K / V codes
-  u32x4 krs, vrs = {}, k8rs = {}, v8rs = {};
+  __amdgpu_buffer_rsrc_t krs, vrs = make_rsrc(nullptr, 0), k8rs = make_rsrc(nullptr, 0),
+                         v8rs = make_rsrc(nullptr, 0);
   uint32_t rs;
   {
     const int64_t krow0 = (int64_t)b * p.k_bs + (int64_t)sb.k_start * p.k_rs +
                           (int64_t)kvh * p.k_hs;
     const uint32_t bytes = sat_bytes((int64_t)sb.Lk * p.k_rs * 2);
-    krs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k) + krow0 * 2, bytes);
-    if constexpr (!E8) vrs = rsrc_words(reinterpret_cast<const uint8_t*>(p.v) + krow0 * 2, bytes);
+    krs = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + krow0 * 2, bytes);
+    if constexpr (!E8) vrs = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + krow0 * 2, bytes);
     rs = (uint32_t)(p.k_rs * 2);
     if constexpr (E8) {
       const uint32_t bytes8 = sat_bytes((int64_t)sb.Lk * p.k_rs);
-      k8rs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k8) + krow0, bytes8);
-      v8rs = rsrc_words(reinterpret_cast<const uint8_t*>(p.v8) + krow0, bytes8);
+      k8rs = make_rsrc(reinterpret_cast<const uint8_t*>(p.k8) + krow0, bytes8);
+      v8rs = make_rsrc(reinterpret_cast<const uint8_t*>(p.v8) + krow0, bytes8);
     }
   }
   uint32_t voff[C::CPT];
@@ -764,7 +784,7 @@ void bwd_dq_kernel(BwdParams p) {
       dma_tile16<D>(vbuf, vrs, (uint32_t)(t * 32) * rs, wid, voff);
     } else if (has8) {
       const uint32_t base8 = (uint32_t)(t * 32) * (uint32_t)p.k_rs;
-      const uint32_t l8 = (uint32_t)(uintptr_t)(lds_void*)vbuf + wid * 1024;
+      const uint8_t* l8 = vbuf + wid * 1024;
       dma16(l8, base8 + voff8, k8rs);
       dma16(l8 + T8, base8 + voff8, v8rs);
     }

@@ -278,6 +278,27 @@ __device__ __forceinline__ void store_row_staged8(const FwdParams& p, const Work
   }
 }
 
+// Packed layout: the launch covers n_qtiles * rows_per_wg rows of every
+// sequence (max_seqlen_q, which the caller promises bounds every length).  A
+// longer sequence breaks that promise; its rows beyond the reach are written
+// as NaN (O and LSE) by the workgroup of its first tile, so the broken promise
+// shows in the result instead of leaving whatever the buffers held.
+template <int OUT_ELEM, int D>
+__device__ __forceinline__ void poison_beyond_reach(const FwdParams& p, const Work& w, int h) {
+  const int reach = p.n_qtiles * p.rows_per_wg;
+  if (p.cu_q == nullptr || w.r0 != 0 || w.Lq <= reach) return;
+  const int n = (w.Lq - reach) * D;
+  for (int e = threadIdx.x; e < n; e += kThreads) {
+    const int r = reach + e / D, d = e % D;
+    const int64_t i = (int64_t)(w.q_start + r) * p.o_rs + (int64_t)h * p.o_hs + d;
+    if constexpr (OUT_ELEM == E_F32) reinterpret_cast<float*>(p.o)[i] = __builtin_nanf("");
+    else if constexpr (OUT_ELEM == E_E4M3) reinterpret_cast<uint8_t*>(p.o)[i] = 0x7F;
+    else if constexpr (OUT_ELEM == E_F16) reinterpret_cast<uint16_t*>(p.o)[i] = 0x7E00;
+    else reinterpret_cast<uint16_t*>(p.o)[i] = 0x7FC0;
+    if (d == 0) p.lse[(int64_t)(w.q_start + r) * p.l_rs + (int64_t)h * p.l_hs] = __builtin_nanf("");
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 / f16 kernel
 // ---------------------------------------------------------------------------
@@ -321,14 +342,12 @@ struct Cfg5 {
 // thread's chunk n goes to LDS chunk (wid*CPT + n)*64 + lane, from tile offset
 // voff[n].  The instruction writes LDS only (no register results).
 template <int ELEM, int D, int NKB>
-__device__ __forceinline__ void dma_tile(uint8_t* buf, u32x4 rsrc, uint32_t base, int wid,
+__device__ __forceinline__ void dma_tile(uint8_t* buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t base,
+                                         int wid,
                                          const uint32_t (&voff)[Cfg5<ELEM, D, NKB>::CPT]) {
   using C = Cfg5<ELEM, D, NKB>;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)buf;
 #pragma unroll
-  for (int n = 0; n < C::CPT; ++n) {
-    dma16(lds0 + (wid * C::CPT + n) * 1024, base + voff[n], rsrc);
-  }
+  for (int n = 0; n < C::CPT; ++n) dma16(buf + (wid * C::CPT + n) * 1024, base + voff[n], rsrc);
 }
 
 // Mask the S^T accumulators of the NKB 32-key blocks of a tile starting at key
@@ -393,14 +412,14 @@ void fwd16_kernel(FwdParams p) {
   }
 
   // K/V of this (sequence, kv head): descriptors and per-thread tile offsets
-  u32x4 krs, vrs;
+  __amdgpu_buffer_rsrc_t krs, vrs;
   uint32_t rs;
   {
     const int64_t koff = ((int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs +
                           (int64_t)w.kvh * p.k_hs) * 2;
     const uint32_t bytes = sat_bytes((int64_t)w.Lk * p.k_rs * 2);
-    krs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
-    vrs = rsrc_words(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
+    krs = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
+    vrs = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
     rs = (uint32_t)(p.k_rs * 2);
   }
   uint32_t voff[C::CPT];
@@ -560,6 +579,7 @@ void fwd16_kernel(FwdParams p) {
   static_assert(C::TILE >= 32 * 2 * D, "a K/V buffer holds one wave's O tile");
   uint8_t* stage = wid == 0 ? lk0 : wid == 1 ? lk1 : wid == 2 ? lv0 : lv1;
   store_row_staged<OUT, D>(p, w, h, w.r0 + 32 * wid, ql, hl, st.m, st.l, st.o, stage);
+  poison_beyond_reach<OUT, D>(p, w, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -635,14 +655,13 @@ void fwd8_kernel(FwdParams p) {
   }
 
   // K/V of this (sequence, kv head)
-  u32x4 krs;
-  __amdgpu_buffer_rsrc_t vr;
+  __amdgpu_buffer_rsrc_t krs, vr;
   uint32_t rs;
   {
     const int64_t koff = (int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs +
                          (int64_t)w.kvh * p.k_hs;
     const uint32_t bytes = sat_bytes((int64_t)w.Lk * p.k_rs);
-    krs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
+    krs = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
     vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
     rs = (uint32_t)p.k_rs;
   }
@@ -656,7 +675,7 @@ void fwd8_kernel(FwdParams p) {
   const uint32_t vst1 = (uint32_t)crow * C::VROWB + (uint32_t)(((2 * cch + 1) ^ swz<D>(crow)) * 16);
   auto dma_k = [&](uint8_t* buf, uint32_t base) __attribute__((always_inline)) {
     if (has_chunk) {
-      dma16((uint32_t)(uintptr_t)(lds_void*)buf + wid * 1024, base + kdma, krs);
+      dma16(buf + wid * 1024, base + kdma, krs);
     }
   };
   auto store_v = [&](uint8_t* buf, u32x4 c) __attribute__((always_inline)) {
@@ -804,6 +823,7 @@ void fwd8_kernel(FwdParams p) {
   static_assert(C::KTILE >= 32 * D && C::VTILE >= 32 * D, "a buffer holds a wave's O codes");
   uint8_t* stage = wid == 0 ? lk0 : wid == 1 ? lk1 : wid == 2 ? lv0 : lv1;
   store_row_staged8<D>(p, w, h, w.r0 + 32 * wid, ql, hl, st.m, st.l, st.o, stage);
+  poison_beyond_reach<E_E4M3, D>(p, w, h);
 }
 // ---------------------------------------------------------------------------
 // f32 kernel (v_mfma_f32_32x32x2_f32: exact products, f32 accumulation)
@@ -960,6 +980,7 @@ void fwd32_kernel(FwdParams p) {
   }
 
   store_row<E_F32, D>(p, w, h, qrow, hl, st.m, st.l, st.o);
+  poison_beyond_reach<E_F32, D>(p, w, h);
 }
 
 // ---------------------------------------------------------------------------

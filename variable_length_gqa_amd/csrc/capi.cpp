@@ -107,7 +107,12 @@ int varlen_attention_fwd(const void* q, const void* k, const void* v,
   if (total_q > INT32_MAX || total_k > INT32_MAX)
     return fail(VLGQA_EINVAL, "total_q", "token counts must fit I32 cu_seqlens");
   if (batch_size > INT32_MAX - 1) return fail(VLGQA_EINVAL, "batch_size", "too large");
-  if (batch_size == 0 || total_q == 0 || max_seqlen_q == 0) return VLGQA_OK;
+  if (batch_size == 0 || total_q == 0) return VLGQA_OK;
+  // lengths at most max_seqlen add up to at most batch_size * max_seqlen
+  if (total_q > batch_size * max_seqlen_q)
+    return fail(VLGQA_EINVAL, "max_seqlen_q", "below total_q / batch_size: a sequence is longer");
+  if (total_k > batch_size * max_seqlen_k)
+    return fail(VLGQA_EINVAL, "max_seqlen_k", "below total_k / batch_size: a sequence is longer");
   if ((rc = check_span(max_seqlen_q, num_heads * head_dim * elem_bytes(elem), "max_seqlen_q")))
     return rc;
   if ((rc = check_span(max_seqlen_k, num_kv_heads * head_dim * elem_bytes(elem),
@@ -353,6 +358,10 @@ int varlen_attention_bwd(const void* dout, const void* q, const void* k, const v
     return fail(VLGQA_EINVAL, "max_seqlen_q", "too large");
   if (batch_size > INT32_MAX - 1) return fail(VLGQA_EINVAL, "batch_size", "too large");
   if (batch_size == 0 || (total_q == 0 && total_k == 0)) return VLGQA_OK;
+  if (total_q > batch_size * max_seqlen_q)
+    return fail(VLGQA_EINVAL, "max_seqlen_q", "below total_q / batch_size: a sequence is longer");
+  if (total_k > batch_size * max_seqlen_k)
+    return fail(VLGQA_EINVAL, "max_seqlen_k", "below total_k / batch_size: a sequence is longer");
   if (dtype == VLGQA_F32)
     return fail(VLGQA_EUNSUPPORTED, "dtype", "the backward is compiled for bf16 and f16 only");
   if ((rc = check_span(max_seqlen_q, num_heads * head_dim * 2, "max_seqlen_q"))) return rc;

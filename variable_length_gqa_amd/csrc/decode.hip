@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "decode_params.h"
 #include "kernel_common.h"
 
@@ -51,8 +53,27 @@ struct CfgD {
 template <int ELEM, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void decode_kernel(DecParams p) {
   using C = CfgD<D>;
-  // ring of NBUF (K, V) tile pairs: NBUF - 1 tiles stream in while one is used
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::NBUF * C::TILE];
+  // ring of three (K, V) tile pairs: two tiles stream in while one is used.
+  // Each buffer is an array of its own and the loop is unrolled over the ring,
+  // so every DMA and every read names its buffer at compile time and the
+  // compiler holds a read back only for the DMA into that same buffer.
+  static_assert(C::NBUF == 3, "the ring is unrolled for three slots");
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv2[C::TILE];
+  auto kbuf = [&](auto U) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(U)::value == 0) return lk0;
+    else if constexpr (decltype(U)::value == 1) return lk1;
+    else return lk2;
+  };
+  auto vbuf = [&](auto U) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(U)::value == 0) return lv0;
+    else if constexpr (decltype(U)::value == 1) return lv1;
+    else return lv2;
+  };
 
   const int np = p.n_parts;
   const int part = blockIdx.x % np;
@@ -90,8 +111,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void decode_kern
 
   const int64_t koff = ((int64_t)b * p.k_bs + (int64_t)kvh * p.k_hs) * 2;
   const uint32_t bytes = sat_bytes((int64_t)n * p.k_rs * 2);
-  const u32x4 krs = rsrc_words(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
-  const u32x4 vrs = rsrc_words(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
   const uint32_t rs = (uint32_t)(p.k_rs * 2);
   uint32_t voff[C::CPL];
 #pragma unroll
@@ -100,13 +121,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void decode_kern
     const int row = P / C::CPR, ch = (P % C::CPR) ^ swz<D>(row);
     voff[c] = (uint32_t)row * rs + ch * 16;
   }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
-  auto dma = [&](int t, int u) __attribute__((always_inline)) {
+  auto dma = [&](int t, auto U) __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)(t * 32) * rs;
+    uint8_t* kb = kbuf(U);
+    uint8_t* vb = vbuf(U);
 #pragma unroll
     for (int c = 0; c < C::CPL; ++c) {
-      dma16(lds0 + (2 * u) * C::TILE + c * 1024, base + voff[c], krs);
-      dma16(lds0 + (2 * u + 1) * C::TILE + c * 1024, base + voff[c], vrs);
+      dma16(kb + c * 1024, base + voff[c], krs);
+      dma16(vb + c * 1024, base + voff[c], vrs);
     }
   };
   const uint32_t koff0 = (uint32_t)ql * C::ROWB + (uint32_t)((hl ^ swz<D>(ql)) * 16);
@@ -129,22 +151,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void decode_kern
   for (int i = 0; i < C::NOB; ++i) o[i] = f32x16{};
 
   constexpr int NB = C::NBUF;
-#pragma unroll
-  for (int i = 0; i < NB - 1; ++i)
-    if (t0 + i < t1) dma(t0 + i, i);
-  for (int t = t0; t < t1; ++t) {
-    const int u = (t - t0) % NB;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  if (t0 < t1) dma(t0, S0{});
+  if (t0 + 1 < t1) dma(t0 + 1, S1{});
+  // tile t sits in slot U = (t - t0) % 3
+  auto step = [&](int t, auto U) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
     // refill the slot used by tile t - 1; then tile t is the oldest of the
     // (up to) NB DMA batches in flight
     if (t + NB - 1 < t1) {
-      dma(t + NB - 1, (u + NB - 1) % NB);
+      dma(t + NB - 1, std::integral_constant<int, (u + NB - 1) % NB>{});
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * 2 * C::CPL));
     } else {
       wait_vm_all();
     }
     asm volatile("" ::: "memory");
-    const uint8_t* kb_ = lds + (2 * u) * C::TILE;
-    const uint8_t* vb_ = lds + (2 * u + 1) * C::TILE;
+    const uint8_t* kb_ = kbuf(U);
+    const uint8_t* vb_ = vbuf(U);
     f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < C::NS; ++ks)
@@ -209,7 +234,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void decode_kern
                              pk[t2], o[db]);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of slot u done before its refill
+  };
+  int t = t0;
+  for (; t + 2 < t1; t += NB) {
+    step(t, S0{});
+    step(t + 1, S1{});
+    step(t + 2, S2{});
   }
+  if (t < t1) step(t, S0{});
+  if (t + 1 < t1) step(t + 1, S1{});
 
   // partial of this wave: unnormalised O (f32), reference max m (log2), l
   l = swap_halves_sum(l);

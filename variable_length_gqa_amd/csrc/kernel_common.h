@@ -160,34 +160,16 @@ __device__ __forceinline__ void lds_barrier() {
 // wait until no vector-memory request of this wave is outstanding
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Raw buffer descriptor words (base, stride 0, byte range, gfx9 flags).
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  u32x4 r = {(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
-  return r;
-}
-
 // Request one 16-byte chunk per lane from global memory (buffer descriptor
 // rsrc, byte offset voff) straight into LDS: lane i writes LDS bytes
-// lds_dst + 16 i .. + 16 (lds_dst is wave-uniform).  The instruction has no
-// register results; it is written out so the compiler does not track it (it
-// cannot tell the LDS buffers apart and would stall every LDS read on it);
-// completion is awaited with an explicit vmcnt wait.  The LDS address goes in
-// m0, which the compiler reserves and warns about clobbering: no instruction
-// these kernels use reads m0 (gfx950 LDS reads and writes take their address
-// from a VGPR, and there is no indexed register access), so only these
-// statements set and use it.
-__device__ __forceinline__ void dma16(uint32_t lds_dst, uint32_t voff, u32x4 rsrc) {
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_dst);
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(dst), "v"(voff), "s"(rsrc)
-      : "memory", "m0");
+// lds_dst + 16 i .. + 16 (lds_dst is wave-uniform: it goes to m0, which the
+// compiler sets).  No register results; completion is awaited with an explicit
+// vmcnt wait before the barrier that publishes the tile.  The compiler tracks
+// the LDS write per __shared__ array, so reads of the other buffers of a
+// double-buffered pair are not held up by it.
+__device__ __forceinline__ void dma16(const void* lds_dst, uint32_t voff,
+                                      __amdgpu_buffer_rsrc_t rsrc) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, (int)voff, 0, 0, 0);
 }
 
 // one V^T operand (32 d x 16 keys) by two transposing reads
