@@ -147,6 +147,31 @@ int flash_attention_decode(const void* q, const void* k, const void* v,
                            int dtype, void* out, float* lse, float* workspace,
                            int64_t workspace_floats, void* hip_stream);
 
+/*
+ * flash_attention_decode without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments (minus the workspace),
+ * kernels, results and errors as flash_attention_decode; the slices' partials
+ * go to a library-owned static device array of 4194304 floats (16 MiB) per
+ * GPU, held until the process ends.  The call allocates nothing (no hipMalloc,
+ * no library routine that allocates): the array's device address is looked up
+ * once per device on the first call there.
+ *
+ *   Limit: vlgqa_decode_workspace_floats(batch, num_kv_heads, head_dim, n)
+ *   must not exceed 4194304; beyond it the call returns EINVAL ("batch: ...")
+ *   without launching.  (About 2.7 M floats for any batch * num_kv_heads up to
+ *   640 at head_dim 128, 1280 at 64.)
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (different streams, or different host threads) race and must be
+ *   ordered by the caller, e.g. on one stream.  EHIP if the array's address
+ *   cannot be found on the current device.
+ */
+int flash_attention_decode_noalloc(const void* q, const void* k, const void* v,
+                                   int64_t batch, int64_t num_heads, int64_t num_kv_heads,
+                                   int64_t seqlen_q, int64_t kv_capacity, int64_t head_dim,
+                                   int causal, int64_t window_size, int64_t kv_seq_len,
+                                   int dtype, void* out, float* lse, void* hip_stream);
+
 /* Workspace floats flash_attention_decode needs for an attended length kv_len
  * (-1 for a negative argument).  Host-only arithmetic. */
 int64_t vlgqa_decode_workspace_floats(int64_t batch, int64_t num_kv_heads, int64_t head_dim,

@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
     for n in ("varlen_attention_fwd", "flash_attention_fwd", "flash_attention_fwd_fp8",
               "varlen_attention_bwd", "flash_attention_bwd", "flash_attention_decode",
               "vlgqa_decode_workspace_floats", "flash_attention_bwd_fp8",
-              "vlgqa_bwd_workspace_floats", "vlgqa_last_error",
+              "vlgqa_bwd_workspace_floats", "flash_attention_decode_noalloc", "vlgqa_last_error",
               "vlgqa_version"):
         assert n in names
 
@@ -382,3 +382,18 @@ def test_sequences_past_32bit_buffer_offsets_are_rejected(lib):
     assert err(lib).startswith("kv_seq_len:"), err(lib)
     assert bwd8(lib, b=1, sq=64, sk=1 << 24) == EINVAL
     assert err(lib).startswith("seqlen_k:"), err(lib)
+
+
+def test_noalloc_decode_rejects_on_the_host(lib):
+    # beyond the 4194304-float static scratch: 2048 x 8 (batch, kv head)
+    # pairs need 16384 * 32 * 130 floats; checked before any HIP call
+    assert lib.flash_attention_decode_noalloc(A, A, A, 2048, 64, 8, 1, 8192, 128, 1, 0, 8192,
+                                              BF16, A, A, None) == EINVAL
+    assert err(lib).startswith("batch:"), err(lib)
+    assert lib.flash_attention_decode_noalloc(A, A, A, 2, 64, 8, 8, 8192, 128, 1, 0, 8192,
+                                              BF16, A, A, None) == EINVAL
+    assert err(lib).startswith("seqlen_q:"), err(lib)
+    assert lib.flash_attention_decode_noalloc(A, A, A, 2, 64, 8, 1, 8192, 128, 1, 0, 8192,
+                                              F32, A, A, None) == EUNSUP
+    assert lib.flash_attention_decode_noalloc(A, A, A, 0, 64, 8, 1, 8192, 128, 1, 0, 8192,
+                                              BF16, 0, 0, None) == _lib.VLGQA_OK

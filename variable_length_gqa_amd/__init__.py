@@ -5,6 +5,7 @@ Entry points (HIP kernels for gfx950 behind a C ABI, see include/vlgqa.h):
   flash_attention_fwd      dense [B, H, S, D], KV capacity stride, sliding window
   flash_attention_fwd_fp8  dense OCP E4M3 with per-tensor scales
   flash_attention_decode   dense, few queries against a long KV cache (split-KV)
+  flash_attention_decode_noalloc  the same without a workspace (library scratch)
       -> (output, logsumexp)
   varlen_attention_bwd     gradients of the packed forward
   flash_attention_bwd      gradients of the dense forward
@@ -19,6 +20,7 @@ from .attention import (  # noqa: F401
     flash_attention_bwd,
     flash_attention_bwd_fp8,
     flash_attention_decode,
+    flash_attention_decode_noalloc,
     flash_attention_fwd,
     flash_attention_fwd_fp8,
     varlen_attention_bwd,

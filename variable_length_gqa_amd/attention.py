@@ -199,6 +199,39 @@ def flash_attention_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nu
     return out, lse
 
 
+def flash_attention_decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                   num_heads: int, num_kv_heads: int, head_dim: int, causal: bool,
+                                   window_size: int, kv_seq_len: int | None, out: torch.Tensor,
+                                   lse: torch.Tensor):
+    """flash_attention_decode for callers that cannot allocate: the split-KV
+    partials go to the library's static per-GPU scratch instead of a workspace,
+    and ``out`` / ``lse`` must be given (nothing is allocated here either).
+    Calls that overlap on one GPU share that scratch and race: order them."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse)):
+        _check_device_tensor(name, t, dev)
+    _need(q.dtype in (torch.bfloat16, torch.float16), f"unsupported dtype {q.dtype}")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share one dtype")
+    _need(q.dim() == 4 and q.shape[1] == num_heads and q.shape[3] == head_dim,
+          "q must be [B, num_heads, S_q, head_dim]")
+    _need(k.dim() == 4 and k.shape[0] == q.shape[0] and k.shape[1] == num_kv_heads
+          and k.shape[3] == head_dim, "k must be [B, num_kv_heads, capacity, head_dim]")
+    _need(v.shape == k.shape, "v must have the shape of k")
+    B, _, Sq, _ = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(lse.shape == (B, num_heads, Sq) and lse.dtype == torch.float32,
+          "lse must be float32 [B, num_heads, S_q]")
+    lib = _lib.load()
+    rc = lib.flash_attention_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), B, num_heads, num_kv_heads,
+                                            Sq, k.shape[2], head_dim, int(bool(causal)),
+                                            int(window_size),
+                                            -1 if kv_seq_len is None else int(kv_seq_len),
+                                            _DTYPE_CODE[q.dtype], _ptr(out), _ptr(lse),
+                                            _stream(dev))
+    _lib.check(rc)
+    return out, lse
+
+
 def flash_attention_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_heads: int,
                             num_kv_heads: int, head_dim: int, causal: bool, q_scale: float,
                             k_scale: float, v_scale: float, o_scale: float,

@@ -234,12 +234,14 @@ int64_t vlgqa_decode_workspace_floats(int64_t batch, int64_t num_kv_heads, int64
   return vlgqa::decode_workspace_floats(batch, num_kv_heads, head_dim, kv_len);
 }
 
-int flash_attention_decode(const void* q, const void* k, const void* v, int64_t batch,
-                           int64_t num_heads, int64_t num_kv_heads, int64_t seqlen_q,
-                           int64_t kv_capacity, int64_t head_dim, int causal, int64_t window_size,
-                           int64_t kv_seq_len, int dtype, void* out, float* lse, float* workspace,
-                           int64_t workspace_floats, void* hip_stream) {
-  g_last_error.clear();
+// The decode path behind flash_attention_decode (caller workspace) and
+// flash_attention_decode_noalloc (workspace == nullptr: the library's static
+// scratch, no allocation).
+static int decode_common(const void* q, const void* k, const void* v, int64_t batch,
+                         int64_t num_heads, int64_t num_kv_heads, int64_t seqlen_q,
+                         int64_t kv_capacity, int64_t head_dim, int causal, int64_t window_size,
+                         int64_t kv_seq_len, int dtype, void* out, float* lse, float* workspace,
+                         int64_t workspace_floats, bool static_scratch, void* hip_stream) {
   int rc, elem = 0;
   if ((rc = elem_of_dtype(dtype, &elem))) return rc;
   if (elem == vlgqa::E_F32)
@@ -266,9 +268,15 @@ int flash_attention_decode(const void* q, const void* k, const void* v, int64_t 
   const int64_t parts = vlgqa::decode_parts(batch, num_kv_heads, head_dim, n);
   if (batch * num_kv_heads * parts > INT32_MAX)
     return fail(VLGQA_EINVAL, "batch", "batch * num_kv_heads too large for one launch");
-  if (workspace_floats < need)
+  if (static_scratch) {
+    if (need > vlgqa::kDecodeScratchFloats)
+      return fail(VLGQA_EINVAL, "batch",
+                  "the slices' partials exceed the library's static decode scratch of 4194304 "
+                  "floats (use flash_attention_decode with a workspace)");
+  } else if (workspace_floats < need) {
     return fail(VLGQA_EINVAL, "workspace_floats",
                 "smaller than vlgqa_decode_workspace_floats(batch, num_kv_heads, head_dim, n)");
+  }
   if ((rc = check_ptr(q, "q"))) return rc;
   if (n > 0) {
     if ((rc = check_ptr(k, "k"))) return rc;
@@ -276,7 +284,12 @@ int flash_attention_decode(const void* q, const void* k, const void* v, int64_t 
   }
   if ((rc = check_ptr(out, "out"))) return rc;
   if ((rc = check_ptr(lse, "lse"))) return rc;
-  if ((rc = check_ptr(workspace, "workspace"))) return rc;
+  if (static_scratch) {
+    hipError_t se = vlgqa::decode_scratch(&workspace);
+    if (se != hipSuccess) return fail(VLGQA_EHIP, "scratch", hipGetErrorString(se));
+  } else if ((rc = check_ptr(workspace, "workspace"))) {
+    return rc;
+  }
 
   vlgqa::DecParams p{};
   p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse; p.ws = workspace;
@@ -298,6 +311,28 @@ int flash_attention_decode(const void* q, const void* k, const void* v, int64_t 
                                       reinterpret_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
   return VLGQA_OK;
+}
+
+int flash_attention_decode(const void* q, const void* k, const void* v, int64_t batch,
+                           int64_t num_heads, int64_t num_kv_heads, int64_t seqlen_q,
+                           int64_t kv_capacity, int64_t head_dim, int causal, int64_t window_size,
+                           int64_t kv_seq_len, int dtype, void* out, float* lse, float* workspace,
+                           int64_t workspace_floats, void* hip_stream) {
+  g_last_error.clear();
+  return decode_common(q, k, v, batch, num_heads, num_kv_heads, seqlen_q, kv_capacity, head_dim,
+                       causal, window_size, kv_seq_len, dtype, out, lse, workspace,
+                       workspace_floats, false, hip_stream);
+}
+
+int flash_attention_decode_noalloc(const void* q, const void* k, const void* v, int64_t batch,
+                                   int64_t num_heads, int64_t num_kv_heads, int64_t seqlen_q,
+                                   int64_t kv_capacity, int64_t head_dim, int causal,
+                                   int64_t window_size, int64_t kv_seq_len, int dtype, void* out,
+                                   float* lse, void* hip_stream) {
+  g_last_error.clear();
+  return decode_common(q, k, v, batch, num_heads, num_kv_heads, seqlen_q, kv_capacity, head_dim,
+                       causal, window_size, kv_seq_len, dtype, out, lse, nullptr, 0, true,
+                       hip_stream);
 }
 
 static int bwd_common(vlgqa::BwdParams& p, int dtype, int64_t head_dim, int64_t rows,

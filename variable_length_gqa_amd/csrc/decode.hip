@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "decode_params.h"
@@ -371,6 +372,42 @@ int64_t decode_workspace_floats(int64_t batch, int64_t kv_heads, int64_t head_di
                                 int64_t kv_len) {
   const int64_t np = decode_parts(batch, kv_heads, head_dim, kv_len);
   return batch * kv_heads * np * 32 * (head_dim + 2);
+}
+
+// ---------------------------------------------------------------------------
+// library-owned scratch for callers that cannot allocate
+// ---------------------------------------------------------------------------
+//
+// The allocation-free decode entry point keeps the slices' partials here
+// instead of in a caller workspace: a file-scope device array, one copy per
+// GPU, alive until the process ends.  Its host-side name is not a device
+// address; the device address is looked up once per device (with that device
+// current) and kept.  Every call on a GPU shares that GPU's copy, so calls
+// that overlap on one GPU race.  Nothing in it needs clearing: the merge reads
+// only partials the same call's slices wrote.
+static __device__ __align__(256) float scratch[kDecodeScratchFloats];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(a);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecParams& p, int elem, int head_dim, hipStream_t stream) {

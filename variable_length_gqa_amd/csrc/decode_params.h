@@ -32,4 +32,10 @@ int64_t decode_workspace_floats(int64_t batch, int64_t kv_heads, int64_t head_di
                                 int64_t kv_len);
 hipError_t launch_decode(const DecParams& p, int elem, int head_dim, hipStream_t stream);
 
+// floats in the library-owned decode scratch (16 MiB per GPU)
+constexpr int64_t kDecodeScratchFloats = (int64_t)4 << 20;
+// device address of the current GPU's copy of that scratch (looked up once per
+// device); no allocation
+hipError_t decode_scratch(float** ptr);
+
 }  // namespace vlgqa
