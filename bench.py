@@ -285,7 +285,8 @@ def cpu_baseline_pack(x, which, padded_dev):
     row = padded[0, 0].nbytes
     nbytes = 2 * packed.shape[0] * row if which == "pack" else \
         packed.shape[0] * row + padded.shape[0] * padded.shape[1] * row
-    return {"value": nbytes / secs / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": nbytes / secs / 1e9, "unit": "GB/s", "cores": 1, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"the whole workload's q ({nbytes / 1e6:.0f} MB moved, {secs:.2f} s, "
                       f"NumPy, one thread)"}
 
@@ -335,10 +336,24 @@ def cpu_baseline_bwd(name, x, n_heads, unit_scale):
     secs = time.perf_counter() - t0
     which = "of batch entry 0" if x.scales else "of every sequence"
     return secs, {"value": fl / secs / unit_scale, "unit": "TFLOP/s", "cores": workers,
-                  "kind": "oracle",
+                  "cpu_model": cpu_model(), "kind": "oracle",
                   "sample": f"backward of query heads 0..{n_heads - 1} of {x.num_heads} {which} "
                             f"({fl:.3e} algorithmic FLOPs, {secs:.1f} s wall, f64 "
                             f"NumPy, one process per core, masked scores computed too)"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 def _fp8_o_scale():
@@ -375,10 +390,65 @@ def cpu_baseline(name, x, n_heads, unit_scale):
         fl = F.attention_flops([Sq] * B, [n] * B, n_heads, D, x.causal, x.window)
     secs = time.perf_counter() - t0
     return secs, {"value": fl / secs / unit_scale, "unit": "TFLOP/s", "cores": workers,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"query heads 0..{n_heads - 1} of {x.num_heads} of every sequence "
                       f"({fl:.3e} algorithmic FLOPs, {secs:.1f} s wall, f64 NumPy, "
                       f"one process per core, masked scores computed too)"}
+
+
+# the other forward workloads timed beside the headline one (every config the
+# metric's target names: f32 MHA, the 16-sequence GQA mix, the dense window
+# over a capacity buffer, FP8)
+OTHER_FORWARD_WORKLOADS = ("varlen_f32_mha", "varlen_bf16_gqa", "dense_bf16_window", "dense_fp8")
+
+
+def W_workload(name):
+    from variable_length_gqa_amd import workloads as W
+
+    return W.workload(name)
+
+
+SETTLE = {"steps": 0, "ms": 0.0}
+
+
+def settle(torch, step, settle_ms):
+    """Untimed steps until the GPU has run the step for about ``settle_ms`` of
+    wall time: from idle its clocks take some 50-100 ms of sustained load to
+    reach their steady state (measured: the long-context forward runs 1.57 ms
+    per step in its first five launches, 1.355 in the next twenty, 1.32 after
+    ~60 ms), which a few warm-up steps do not cover.  Recorded in the JSON line
+    ("settle") beside the W warm-up steps."""
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(4):
+            step()
+        n += 4
+        torch.cuda.synchronize()
+    SETTLE["steps"] += n
+    SETTLE["ms"] += (time.perf_counter() - t0) * 1e3
+    return n
+
+
+def time_steps(torch, step, steps, warmup, dev, settle_ms=150.0):
+    """Clock settle (untimed), W untimed warm-up steps, then K steps between HIP
+    events recorded on torch's current stream (the stream every entry point
+    launches on), bracketed by device synchronisation.  Returns (ms per step,
+    wall s)."""
+    if settle_ms > 0:
+        settle(torch, step, settle_ms)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
 
 
 def main():
@@ -388,6 +458,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="varlen_bf16_long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="untimed steps for about this long before the warm-up steps, so "
+                         "the GPU clocks reach their steady state under load (0: none)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="time only the named workload (by default the long-context forward "
+                         "run also times the other forward workloads)")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="query heads in the CPU-baseline sample (0: sized to ~15 s)")
     ap.add_argument("--pass", dest="which",
@@ -427,21 +503,7 @@ def main():
     if args.which == "decode":
         return bench_decode(args, dev)
     x, step, flops, io, cfg, dt = (make_step_bwd if bwd else make_step)(args.workload, dev)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms, wall = time_steps(torch, step, args.steps, args.warmup, dev, args.settle_ms)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dt]
     traffic = measured_traffic(args.workload, args.which)
@@ -456,11 +518,31 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
         "flops_per_step": flops, "wall_s_timed": round(wall, 3),
+        "settle": {"steps": SETTLE["steps"], "ms": round(SETTLE["ms"], 1),
+                   "note": "untimed steps before the warm-up ones, for steady GPU clocks"},
         "kernel_source_digest": kernel_source_digest(args.which),
     }
     if io is not None:
         res["io_bytes_per_step"] = io
         res["io_gbs"] = round(io / (ms * 1e-3) / 1e9, 1)
+    if not bwd and not args.no_workloads and args.workload == "varlen_bf16_long":
+        # the other forward workloads, each timed exactly as the headline one
+        # (its own W warm-up steps, then K timed steps on the kernel's stream)
+        del x, step
+        torch.cuda.empty_cache()
+        res["workloads"] = {}
+        for name in OTHER_FORWARD_WORKLOADS:
+            xo, so, fo, _, co, do = make_step(name, dev)
+            mso, _ = time_steps(torch, so, args.steps, args.warmup, dev, args.settle_ms)
+            tf = fo / (mso * 1e-3) / 1e12
+            pk = PEAK_TFLOPS[do]
+            res["workloads"][name] = {
+                "ms_per_step": round(mso, 4), "tflops": round(tf, 2), "dtype": do,
+                "peak_tflops": pk, "frac": round(tf / pk, 4), "flops_per_step": fo,
+                "traffic": measured_traffic(name, "forward"), "config": co}
+            del xo, so
+            torch.cuda.empty_cache()
+        x = W_workload(args.workload)
     if not args.no_cpu_baseline:
         base = cpu_baseline_bwd if bwd else cpu_baseline
         n_heads = args.cpu_heads
@@ -477,19 +559,11 @@ def bench_pack(args, dev):
     import torch
 
     x, step, nbytes, padded, cfg, dt = make_step_pack(args.workload, dev, args.which)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    ms, _ = time_steps(torch, step, args.steps, args.warmup, dev, args.settle_ms)
+    gbs = nbytes / (ms * 1e-3) / 1e9
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    gbs = nbytes / (ms * 1e-3) / 1e9
     # reference: a plain device-to-device copy moving the same bytes (half read, half written)
     src = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -511,6 +585,7 @@ def bench_pack(args, dev):
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload, args.which)},
         "bytes_per_step": nbytes, "copy_reference_gbs": round(copy_gbs, 1),
+        "settle": {"steps": SETTLE["steps"], "ms": round(SETTLE["ms"], 1)},
         "kernel_source_digest": kernel_source_digest("pack"),
     }
     if not args.no_cpu_baseline:
@@ -543,7 +618,8 @@ def cpu_baseline_decode(x):
                                x.kv_seq_len, workers=workers)
     secs = time.perf_counter() - t0
     nb = decode_bytes(x)
-    return {"value": nb / secs / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+    return {"value": nb / secs / 1e9, "unit": "GB/s", "cores": workers, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"the whole workload ({nb / 1e6:.0f} MB of algorithmic traffic, "
                       f"{secs:.1f} s wall, f64 NumPy, one process per core)"}
 
@@ -572,20 +648,7 @@ def bench_decode(args, dev):
         vg.flash_attention_decode(dd.q, dd.k, dd.v, H, x.num_kv_heads, D, x.causal, x.window,
                                   x.kv_seq_len, out=out, lse=lse, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms, wall = time_steps(torch, step, args.steps, args.warmup, dev, args.settle_ms)
     nb = decode_bytes(x)
     gbs = nb / (ms * 1e-3) / 1e9
     flops = F.attention_flops([Sq] * B, [n] * B, H, D, x.causal, x.window)
@@ -602,7 +665,9 @@ def bench_decode(args, dev):
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(name, "decode")},
         "bytes_per_step": nb, "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
-        "wall_s_timed": round(wall, 3), "kernel_source_digest": kernel_source_digest("decode"),
+        "wall_s_timed": round(wall, 3),
+        "settle": {"steps": SETTLE["steps"], "ms": round(SETTLE["ms"], 1)},
+        "kernel_source_digest": kernel_source_digest("decode"),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(x)
