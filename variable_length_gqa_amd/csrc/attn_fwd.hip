@@ -108,6 +108,34 @@ __device__ __forceinline__ void key_range(const FwdParams& p, const Work& w, int
   lo = p.window > 0 ? max(0, qa + off - p.window + 1) : 0;
 }
 
+// The BN-key tiles a wave of 32 query rows (rows rw .. rw + 31 of the
+// workgroup's tile) works on, [tv0, tv1) (empty when the wave has no rows),
+// and which of them need element masks: tiles below tm_lo the window's lower
+// bound, tiles from tm_hi on the causal bound or the sequence end.  Computed
+// once, so a tile's tests are two integer compares each.
+__device__ __forceinline__ void wave_tiles(const FwdParams& p, const Work& w, int rw, int BN,
+                                           int& tv0, int& tv1, int& tm_lo, int& tm_hi) {
+  const int wa = w.r0 + rw, wb = min(wa + 31, w.Lq - 1);
+  const int off = w.Lk - w.Lq;
+  const bool upper = p.causal || p.window > 0;
+  tv0 = tv1 = 0;
+  if (wa <= wb) {
+    int lo, hi;
+    key_range(p, w, wa, wb, lo, hi);
+    if (hi > lo) {
+      tv0 = lo / BN;
+      tv1 = (hi + BN - 1) / BN;
+    }
+  }
+  // key c of a tile is unmasked for every row of the wave iff c <= lim (the
+  // first row's causal bound, or the last key) and c >= wlim (the last row's
+  // window start)
+  const int lim = upper ? min(w.Lk - 1, wa + off) : w.Lk - 1;
+  tm_hi = lim >= 0 ? (lim + 1) / BN : 0;
+  const int wlim = wb + off - p.window + 1;
+  tm_lo = p.window > 0 && wlim > 0 ? (wlim + BN - 1) / BN : 0;
+}
+
 // ---------------------------------------------------------------------------
 // shared softmax / epilogue pieces
 // ---------------------------------------------------------------------------
@@ -346,8 +374,10 @@ __device__ __forceinline__ void dma_tile(uint8_t* buf, __amdgpu_buffer_rsrc_t rs
                                          int wid,
                                          const uint32_t (&voff)[Cfg5<ELEM, D, NKB>::CPT]) {
   using C = Cfg5<ELEM, D, NKB>;
+  // the tile's base goes in the scalar offset: no per-tile vector add
+  const uint32_t sb = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
-  for (int n = 0; n < C::CPT; ++n) dma16(buf + (wid * C::CPT + n) * 1024, base + voff[n], rsrc);
+  for (int n = 0; n < C::CPT; ++n) dma16(buf + (wid * C::CPT + n) * 1024, voff[n], rsrc, sb);
 }
 
 // Mask the S^T accumulators of the NKB 32-key blocks of a tile starting at key
@@ -456,9 +486,8 @@ void fwd16_kernel(FwdParams p) {
   key_range(p, w, w.r0, min(w.r0 + p.rows_per_wg, w.Lq) - 1, kv_lo, kv_hi);
   const int t0 = kv_lo / BN;
   const int t1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : t0;
-  const int wa = w.r0 + 32 * wid, wb = min(wa + 31, w.Lq - 1);
-  int wlo = 0, whi = 0;
-  if (wa <= wb) key_range(p, w, wa, wb, wlo, whi);
+  int tv0, tv1, tm_lo, tm_hi;
+  wave_tiles(p, w, 32 * wid, BN, tv0, tv1, tm_lo, tm_hi);
 
   RowState<C::NOB> st;
   st.m = -INFINITY;
@@ -481,7 +510,7 @@ void fwd16_kernel(FwdParams p) {
       dma_tile<ELEM, D, NKB>(vnext, vrs, base, wid, voff);
     }
     const int c0 = t * BN;
-    if (wa <= wb && c0 < whi && c0 + BN > wlo) {
+    if (t >= tv0 && t < tv1) {
       // S^T = K Q^T for the two 32-key blocks
       f32x16 s[NKB];
 #pragma unroll
@@ -497,9 +526,7 @@ void fwd16_kernel(FwdParams p) {
       }
       // four K fragment reads in flight ahead of the products (+1% measured)
       if constexpr (NKB == 1) sched_lds_ahead<C::NS, 1, 4>();
-      const bool need_mask = (c0 + BN > w.Lk) || (upper && c0 + BN - 1 > wa + off) ||
-                             (p.window > 0 && c0 < wb + off - p.window + 1);
-      if (need_mask) mask_blocks<NKB>(s, c0, hl, qrow, off, w.Lk, upper, p.window);
+      if (t >= tm_hi || t < tm_lo) mask_blocks<NKB>(s, c0, hl, qrow, off, w.Lk, upper, p.window);
 
       // Online softmax over the row's BN scores (half here, half in lane ^ 32).
       // Optimistic: exponentiate against the current reference maximum and
@@ -675,7 +702,7 @@ void fwd8_kernel(FwdParams p) {
   const uint32_t vst1 = (uint32_t)crow * C::VROWB + (uint32_t)(((2 * cch + 1) ^ swz<D>(crow)) * 16);
   auto dma_k = [&](uint8_t* buf, uint32_t base) __attribute__((always_inline)) {
     if (has_chunk) {
-      dma16(buf + wid * 1024, base + kdma, krs);
+      dma16(buf + wid * 1024, kdma, krs, __builtin_amdgcn_readfirstlane(base));
     }
   };
   auto store_v = [&](uint8_t* buf, u32x4 c) __attribute__((always_inline)) {
@@ -716,9 +743,8 @@ void fwd8_kernel(FwdParams p) {
   key_range(p, w, w.r0, min(w.r0 + p.rows_per_wg, w.Lq) - 1, kv_lo, kv_hi);
   const int t0 = kv_lo / BN;
   const int t1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : t0;
-  const int wa = w.r0 + 32 * wid, wb = min(wa + 31, w.Lq - 1);
-  int wlo = 0, whi = 0;
-  if (wa <= wb) key_range(p, w, wa, wb, wlo, whi);
+  int tv0, tv1, tm_lo, tm_hi;
+  wave_tiles(p, w, 32 * wid, BN, tv0, tv1, tm_lo, tm_hi);
 
   RowState<C::NOB> st;
   st.m = -INFINITY;
@@ -744,7 +770,7 @@ void fwd8_kernel(FwdParams p) {
       if (has_chunk) vc = bload16(vr, base + vld);
     }
     const int c0 = t * BN;
-    if (wa <= wb && c0 < whi && c0 + BN > wlo) {
+    if (t >= tv0 && t < tv1) {
       f32x16 s[1] = {f32x16{}};
 #pragma unroll
       for (int ks = 0; ks < C::NS; ++ks) {
@@ -752,9 +778,7 @@ void fwd8_kernel(FwdParams p) {
                             *reinterpret_cast<const u32x4*>(kb_ + koffs[ks][1])};
         s[0] = mfma_fp8(a, qf[ks], s[0]);
       }
-      const bool need_mask = (c0 + BN > w.Lk) || (upper && c0 + BN - 1 > wa + off) ||
-                             (p.window > 0 && c0 < wb + off - p.window + 1);
-      if (need_mask) mask_blocks<1>(s, c0, hl, qrow, off, w.Lk, upper, p.window);
+      if (t >= tm_hi || t < tm_lo) mask_blocks<1>(s, c0, hl, qrow, off, w.Lk, upper, p.window);
 
       // optimistic softmax, exactly as in the 16-bit kernel
       u32x4 pk[2];

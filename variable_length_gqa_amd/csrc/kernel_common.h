@@ -168,8 +168,10 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 // the LDS write per __shared__ array, so reads of the other buffers of a
 // double-buffered pair are not held up by it.
 __device__ __forceinline__ void dma16(const void* lds_dst, uint32_t voff,
-                                      __amdgpu_buffer_rsrc_t rsrc) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, (int)voff, 0, 0, 0);
+                                      __amdgpu_buffer_rsrc_t rsrc, uint32_t soff = 0) {
+  // soff: a wave-uniform byte offset added in the scalar unit
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, (int)voff, (int)soff, 0,
+                                           0);
 }
 
 // one V^T operand (32 d x 16 keys) by two transposing reads
