@@ -26,6 +26,16 @@
  *     kernels are enqueued on `hip_stream` (a hipStream_t; NULL = the null
  *     stream) and the call returns at once.  Buffers must stay alive until the
  *     stream work completes.
+ *   - Forward launches hand out their last items at run time (faster XCDs
+ *     take more of them) from a claim counter the library owns: one 4-byte
+ *     device counter per (device, stream) a forward has been launched on, zero
+ *     when the library loads, for up to 64 streams per device.  Launches on
+ *     one stream run in order and so never use a counter at the same time;
+ *     the host keeps each counter's running value (a mutex orders the
+ *     launches of several host threads on one stream).  A launch on a stream
+ *     that is being captured into a graph, on hipStreamPerThread, or on a
+ *     65th stream uses the static order instead; results are identical
+ *     either way.
  *   - Base pointers must be 16-byte aligned.
  *   - Return value: VLGQA_OK, or an error code; no exception crosses the ABI.
  *     vlgqa_last_error() then gives "argument: reason" (thread-local, valid

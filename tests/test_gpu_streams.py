@@ -1,6 +1,9 @@
-"""The library keeps no state between calls: forward and backward calls issued
-on two streams at once (each backward with its own workspace) give bit for bit
-the results of the same calls run one after the other."""
+"""Calls on several streams and many calls on one stream: forward and backward
+calls issued on two streams at once (each backward with its own workspace)
+give bit for bit the results of the same calls run one after the other.  The
+forward keeps one claim counter per stream for handing out the last items of
+a launch at run time; repeated launches on one stream (each continuing that
+counter) give bit for bit the same results."""
 
 import pytest
 import torch
@@ -59,3 +62,30 @@ def test_concurrent_calls_on_two_streams_match_sequential():
     for p, w in zip((pa, pb), want):
         for k, v in w.items():
             assert torch.equal(p[2][k], v), k
+
+
+def test_repeated_forward_launches_on_one_stream_are_identical():
+    # large enough that a fifth of every XCD's slots is claimed at run time
+    x = W.make_varlen([2048, 1024, 700, 300, 33], num_heads=32, num_kv_heads=8, head_dim=128,
+                      dtype=torch.bfloat16, causal=True, seed=920).to(DEV)
+    L = max(x.lengths_q)
+    out = torch.empty_like(x.q)
+    lse = torch.empty(x.q.shape[0], 32, dtype=torch.float32, device=DEV)
+
+    def run():
+        out.fill_(float("nan"))
+        vg.varlen_attention_fwd(x.q, x.k, x.v, x.cu_q, x.cu_k, x.batch_size, 32, 8, L, L, 128,
+                                True, out=out, lse=lse)
+        return out.clone(), lse.clone()
+
+    o0, l0 = run()
+    side = torch.cuda.Stream()
+    for i in range(40):
+        if i % 7 == 3:  # now and then a launch on another stream
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                o, l = run()
+            torch.cuda.current_stream().wait_stream(side)
+        else:
+            o, l = run()
+        assert torch.equal(o, o0) and torch.equal(l, l0), i

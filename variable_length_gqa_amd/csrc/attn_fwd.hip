@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 #include "fwd_params.h"
@@ -54,7 +56,11 @@ constexpr float kPartialSumBound = 32768.0f;
 // its G query heads (heads_per_wg at a time) and read the same K/V, so they
 // are placed on consecutive slots of ONE XCD and share its L2.  Groups are
 // ordered by descending query tile: under a causal mask later tiles see more
-// keys, so the longest work is dispatched first.  Under a sliding window the
+// keys, so the longest work is dispatched first.  The XCDs run the same work
+// at different speeds (their finishing times spread by ~9%), so the last
+// slots of every XCD (about a fifth, the shortest items) are not tied to a
+// block: the blocks after the statically assigned ones claim them in order
+// from a counter, and fast XCDs take more of them.  Under a sliding window the
 // tiles of one sequence come together instead (sequence-major, descending
 // within it): nearby tiles read nearly the same window of K/V, and the
 // windows of the sequences interleaved would not fit an XCD's L2 together.
@@ -66,8 +72,23 @@ struct Work {
 __device__ __forceinline__ bool decode_work(const FwdParams& p, Work& w) {
   const int G2 = p.group / p.heads_per_wg;  // workgroups per group
   const int pid = blockIdx.x;
-  const int xcd = pid & 7;
-  const int slot = pid >> 3;
+  int xcd = pid & 7;
+  int slot = pid >> 3;
+  if (p.ticket != nullptr && pid >= 8 * p.n_static) {
+    // a claiming block: its item is the next unclaimed tail item (slot by
+    // slot, XCD by XCD: descending work), so XCDs that run faster take more
+    // of the end of the launch.  A relaxed atomic: only the counter's
+    // atomicity matters (an ordering fence here would write back the L2).
+    __shared__ unsigned claimed;
+    if (threadIdx.x == 0)
+      claimed = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) - p.ticket_base;
+    __syncthreads();
+    const unsigned j = __builtin_amdgcn_readfirstlane(claimed);
+    if (j >= (unsigned)p.n_tail) return false;
+    xcd = (int)(j & 7);
+    slot = p.n_static + (int)(j >> 3);
+  }
   const int gq = slot / G2;
   const int g2 = slot - gq * G2;
   const int grp = gq * 8 + xcd;
@@ -1031,11 +1052,80 @@ bool plan_fwd(FwdParams& p, int elem, int head_dim) {
 #ifndef VLGQA_WPE
 #define VLGQA_WPE 3
 #endif
+constexpr int kTicketSlots = 64;    // streams per device with run-time hand-out
+constexpr int kTicketDevices = 64;
+constexpr int kTailDivisor = 5;     // a fifth of every XCD's slots is claimed at run time
 constexpr int kNkb = VLGQA_NKB;  // 32-key blocks per tile of the bf16/f16 kernel
 constexpr int kWpe = VLGQA_WPE;  // its waves per SIMD (D = 128)
 constexpr int kWpe64 = 4;        // at D = 64 (about 100 VGPRs, 16 KB of LDS a workgroup)
 
-hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t stream) {
+// Claim counters of the run-time hand-out: one per (device, stream) the
+// forward has launched on, library-owned, zero when the code object loads.
+// Each launch claims exactly n_claim times; the host keeps the running count
+// per stream, and launches on one stream run one after the other, so a
+// launch's claims are the counter's next n_claim values (no reset needed).
+static __device__ unsigned fwd_ticket[kTicketSlots * 32];  // 128 bytes apart
+
+namespace {
+std::mutex g_ticket_mutex;  // held from a launch's claim base to its enqueue
+unsigned* g_ticket_base_ptr[kTicketDevices] = {};
+struct TicketSlot {
+  int index;
+  unsigned next;  // the counter's value once the launches enqueued so far have run
+};
+std::map<std::pair<int, hipStream_t>, TicketSlot> g_ticket_slots;
+int g_ticket_used[kTicketDevices] = {};
+
+// The (device, stream) slot, or null when the launch must use the static
+// order: a stream being captured into a graph (it may be replayed on another
+// stream), the per-thread default stream (one handle, many streams), more than
+// kTicketSlots streams on a device.  Caller holds g_ticket_mutex.
+TicketSlot* ticket_slot(hipStream_t stream, int* dev_out) {
+  if (stream == hipStreamPerThread) return nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kTicketDevices) return nullptr;
+  if (!g_ticket_base_ptr[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(fwd_ticket)) != hipSuccess) return nullptr;
+    g_ticket_base_ptr[dev] = static_cast<unsigned*>(a);
+  }
+  auto key = std::make_pair(dev, stream);
+  auto it = g_ticket_slots.find(key);
+  if (it == g_ticket_slots.end()) {
+    if (g_ticket_used[dev] >= kTicketSlots) return nullptr;
+    it = g_ticket_slots.emplace(key, TicketSlot{g_ticket_used[dev]++, 0u}).first;
+  }
+  *dev_out = dev;
+  return &it->second;
+}
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p0, int elem, int head_dim, hipStream_t stream) {
+  FwdParams p = p0;
+  std::unique_lock<std::mutex> lock(g_ticket_mutex, std::defer_lock);
+  TicketSlot* slot = nullptr;
+  {
+    const int G2 = p.group / p.heads_per_wg;
+    const int64_t slots = ((int64_t)p.n_groups + 7) / 8 * G2;  // per XCD
+    const int64_t tail = slots / kTailDivisor;
+    if (tail >= 2 && slots * 8 < INT32_MAX / 2) {
+      lock.lock();
+      int dev = 0;
+      slot = ticket_slot(stream, &dev);
+      if (slot) {
+        p.ticket = g_ticket_base_ptr[dev] + 32 * slot->index;
+        p.ticket_base = slot->next;
+        p.n_static = (int32_t)(slots - tail);
+        p.n_tail = (int32_t)(8 * tail);
+        p.n_claim = (int32_t)(8 * (tail + tail / 10 + 1));  // ~10% spares
+      } else {
+        lock.unlock();
+      }
+    }
+  }
   const int64_t grid = fwd_grid_size(p);
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), b(kThreads);
@@ -1060,7 +1150,10 @@ hipError_t launch_fwd(const FwdParams& p, int elem, int head_dim, hipStream_t st
     return hipErrorInvalidValue;
   }
 #undef VLGQA_LAUNCH
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  // the counter moves only for a launch that was enqueued
+  if (slot && e == hipSuccess) slot->next += (unsigned)p.n_claim;
+  return e;
 }
 
 }  // namespace vlgqa

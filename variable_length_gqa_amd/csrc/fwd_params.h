@@ -37,10 +37,17 @@ struct FwdParams {
   int32_t n_groups;      // n_qtiles * batch * kv_heads
   float score_mul;   // multiplies q.k into the log2 domain: scale * log2(e) [* q_scale * k_scale]
   float out_mul;     // multiplies the normalised output: 1, or v_scale / o_scale for E4M3
+  // run-time hand-out of the last items of a launch (filled by launch_fwd):
+  unsigned* ticket;    // this stream's claim counter, or null: every block's item by its index
+  unsigned ticket_base;  // the counter's value when this launch starts
+  int32_t n_static;    // slots per XCD handed out by block index
+  int32_t n_tail;      // items after them (8 per remaining slot), claimed in order
+  int32_t n_claim;     // blocks that claim one (the tail items plus spares)
 };
 
 // Number of workgroups the forward launch uses for these parameters.
 inline int64_t fwd_grid_size(const FwdParams& p) {
+  if (p.ticket) return 8 * (int64_t)p.n_static + p.n_claim;
   int64_t groups8 = ((int64_t)p.n_groups + 7) / 8 * 8;
   return groups8 * (p.group / p.heads_per_wg);
 }
