@@ -780,6 +780,11 @@ void fwd8_kernel(FwdParams p) {
     store_v(lv0, vc);
   }
   lds_barrier();
+  // nothing is in flight here on any path; saying so keeps the compiler's
+  // wait insertion from carrying the Q code loads into the tile loop as
+  // pending, where it would wait for each tile's prefetch before the
+  // tile's second score MFMA
+  wait_vm_all();
 
   auto tile = [&](int t, const uint8_t* kb_, const uint8_t* vb_, uint8_t* knext,
                   uint8_t* vnext) __attribute__((always_inline)) {

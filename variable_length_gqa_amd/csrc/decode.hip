@@ -123,13 +123,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void decode_kern
     voff[c] = (uint32_t)row * rs + ch * 16;
   }
   auto dma = [&](int t, auto U) __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)(t * 32) * rs;
+    // the tile's base in the scalar offset: no per-tile vector adds
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(t * 32) * rs);
     uint8_t* kb = kbuf(U);
     uint8_t* vb = vbuf(U);
 #pragma unroll
     for (int c = 0; c < C::CPL; ++c) {
-      dma16(kb + c * 1024, base + voff[c], krs);
-      dma16(vb + c * 1024, base + voff[c], vrs);
+      dma16(kb + c * 1024, voff[c], krs, base);
+      dma16(vb + c * 1024, voff[c], vrs, base);
     }
   };
   const uint32_t koff0 = (uint32_t)ql * C::ROWB + (uint32_t)((hl ^ swz<D>(ql)) * 16);
