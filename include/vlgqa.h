@@ -202,8 +202,17 @@ int64_t vlgqa_decode_workspace_floats(int64_t batch, int64_t num_kv_heads, int64
  *   lse    [batch, num_heads, seqlen_q]               float32, over the scaled
  *                              scores q_scale*k_scale*<q8,k8>/sqrt(head_dim)
  *
+ * Two launches on hip_stream: an exact bf16 copy of the V codes (every E4M3
+ * value is a bf16 value), then the attention kernel.  The copy lives in a
+ * block of 2 * batch * num_kv_heads * seqlen_k * head_dim bytes taken, in
+ * stream order, from a device memory pool the library creates per device and
+ * keeps until the process ends (it holds on to what it has reserved, so only
+ * a first call, or a larger one, reserves device memory); the block is given
+ * back on hip_stream after the kernel.
+ *
  * Errors: EINVAL as above, plus any scale that is not finite and positive;
- * EUNSUPPORTED for head_dim not in {64, 128}.
+ * EUNSUPPORTED for head_dim not in {64, 128}; EHIP when the scratch block
+ * cannot be had.
  */
 int flash_attention_fwd_fp8(const void* q, const void* k, const void* v,
                             int64_t batch, int64_t num_heads, int64_t num_kv_heads,

@@ -56,6 +56,7 @@
 
 #include "bwd_params.h"
 #include "kernel_common.h"
+#include "pack_api.h"
 
 namespace vlgqa {
 
@@ -86,20 +87,6 @@ __device__ __forceinline__ int64_t ws_index(const BwdParams& p, int b, int64_t r
 }
 __device__ __forceinline__ int64_t ws_plane(const BwdParams& p) {
   return (int64_t)p.d_batch * p.heads * p.d_rows;
-}
-
-// E4M3 codes -> bf16 copy, 16 codes per thread (n16 = elements / 16)
-__global__ __launch_bounds__(256) void widen_e4m3_kernel(const uint8_t* __restrict__ src,
-                                                         uint16_t* __restrict__ dst, int64_t n16) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n16) return;
-  const u32x4 c = *reinterpret_cast<const u32x4*>(src + i * 16);
-  const u32x4 lo = {fp8x2_to_bf16x2(c[0], false), fp8x2_to_bf16x2(c[0], true),
-                    fp8x2_to_bf16x2(c[1], false), fp8x2_to_bf16x2(c[1], true)};
-  const u32x4 hi = {fp8x2_to_bf16x2(c[2], false), fp8x2_to_bf16x2(c[2], true),
-                    fp8x2_to_bf16x2(c[3], false), fp8x2_to_bf16x2(c[3], true)};
-  *reinterpret_cast<u32x4*>(dst + i * 16) = lo;
-  *reinterpret_cast<u32x4*>(dst + i * 16 + 8) = hi;
 }
 
 // ---------------------------------------------------------------------------
@@ -964,11 +951,10 @@ hipError_t launch_bwd(const BwdParams& p, int elem, int head_dim, hipStream_t st
     // codes)
     const struct { const void* src; void* dst; int64_t n; } w[3] = {
         {p.q8, p.wq, p.n_q}, {p.do8, p.wdo, p.n_q}, {p.k8, p.wk, p.n_k}};
-    for (const auto& t : w)
-      if (t.n > 0)
-        hipLaunchKernelGGL(widen_e4m3_kernel, dim3((unsigned)((t.n / 16 + 255) / 256)), dim3(256),
-                           0, stream, reinterpret_cast<const uint8_t*>(t.src),
-                           reinterpret_cast<uint16_t*>(t.dst), t.n / 16);
+    for (const auto& t : w) {
+      const hipError_t e = launch_widen_e4m3(t.src, t.dst, t.n, stream);
+      if (e != hipSuccess) return e;
+    }
   }
 #define VLGQA_BWD(E, D, E8)                                                    \
   do {                                                                         \

@@ -645,10 +645,12 @@ void fwd16_kernel(FwdParams p) {
 //   P V stays on the bf16 matrix cores with P rounded to bf16: rounding P to
 //     E4M3 instead (3 mantissa bits) moves O by up to ~2.5% of max|O| on
 //     long, flat rows, which with the E4M3 rounding of the output exceeds the
-//     6e-2 * max|O| tolerance.  V codes are loaded to registers one tile ahead,
-//     widened to bf16 (exact: every E4M3 value is a bf16 value) with
-//     v_cvt_scalef32_pk_bf16_fp8, and written to LDS in the 16-bit kernel's
-//     swizzled row layout, so the same transposing reads build V^T.
+//     6e-2 * max|O| tolerance.  V arrives as its bf16 copy (exact: every E4M3
+//     value is a bf16 value), made by a widening launch on the same stream just
+//     before, and reaches LDS by DMA in the 16-bit kernel's swizzled row layout,
+//     so the same transposing reads build V^T.  (Widening each V tile inside
+//     every workgroup that reads it cost ~16 vector instructions per tile and
+//     wave, about a fifth of the kernel's time.)
 // The epilogue multiplies by v_scale / o_scale and encodes E4M3 with round to
 // nearest even, saturating at +-448.
 
@@ -660,7 +662,7 @@ struct Cfg8 {
   static constexpr int KROWB = D;                    // bytes per E4M3 K row in LDS
   static constexpr int KCPR = KROWB / 16;            // 16-byte chunks per K row
   static constexpr int KTILE = BN * KROWB;           // bytes of one K tile
-  static constexpr int NCH = KTILE / 16;             // 16-byte chunks per K (or E4M3 V) tile
+  static constexpr int NCH = KTILE / 16;             // 16-byte chunks per K tile
   static constexpr int VROWB = 2 * D;                // bytes per bf16 V row in LDS
   static constexpr int VTILE = BN * VROWB;           // bytes of one bf16 V tile
   static_assert(NCH <= kThreads && NCH % 64 == 0, "tile shape");
@@ -702,40 +704,37 @@ void fwd8_kernel(FwdParams p) {
     }
   }
 
-  // K/V of this (sequence, kv head)
-  __amdgpu_buffer_rsrc_t krs, vr;
-  uint32_t rs;
+  // K codes and V of this (sequence, kv head).  p.v is the bf16 copy of the V
+  // codes (exact, made by the launch before this one), with the codes'
+  // element strides: V tiles reach LDS by DMA in the 16-bit kernel's layout,
+  // with no vector work.
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  uint32_t rs;  // bytes per K row; a V row has twice as many
   {
     const int64_t koff = (int64_t)w.b * p.k_bs + (int64_t)w.k_start * p.k_rs +
                          (int64_t)w.kvh * p.k_hs;
-    const uint32_t bytes = sat_bytes((int64_t)w.Lk * p.k_rs);
-    krs = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + koff, bytes);
-    vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + koff, bytes);
+    const int64_t bytes = (int64_t)w.Lk * p.k_rs;
+    krs = make_rsrc(reinterpret_cast<const uint8_t*>(p.k) + koff, sat_bytes(bytes));
+    vrs = make_rsrc(reinterpret_cast<const uint8_t*>(p.v) + 2 * koff, sat_bytes(2 * bytes));
     rs = (uint32_t)p.k_rs;
   }
-  // this thread's 16-byte chunk of a K (or E4M3 V) tile, if any (wave-uniform)
+  // this thread's 16-byte chunk of a K tile, if any (wave-uniform)
   const bool has_chunk = wid * 64 < C::NCH;
   const int crow = tid / C::KCPR, cch = tid % C::KCPR;
   const uint32_t kdma = (uint32_t)crow * rs + (uint32_t)((cch ^ swz8<D>(crow)) * 16);
-  const uint32_t vld = (uint32_t)crow * rs + (uint32_t)cch * 16;
-  //  ... whose 16 bf16 go to logical chunks 2 cch, 2 cch + 1 of V row crow
-  const uint32_t vst0 = (uint32_t)crow * C::VROWB + (uint32_t)(((2 * cch) ^ swz<D>(crow)) * 16);
-  const uint32_t vst1 = (uint32_t)crow * C::VROWB + (uint32_t)(((2 * cch + 1) ^ swz<D>(crow)) * 16);
   auto dma_k = [&](uint8_t* buf, uint32_t base) __attribute__((always_inline)) {
     if (has_chunk) {
       dma16(buf + wid * 1024, kdma, krs, __builtin_amdgcn_readfirstlane(base));
     }
   };
-  auto store_v = [&](uint8_t* buf, u32x4 c) __attribute__((always_inline)) {
-    if (has_chunk) {
-      const u32x4 lo = {fp8x2_to_bf16x2(c[0], false), fp8x2_to_bf16x2(c[0], true),
-                        fp8x2_to_bf16x2(c[1], false), fp8x2_to_bf16x2(c[1], true)};
-      const u32x4 hi = {fp8x2_to_bf16x2(c[2], false), fp8x2_to_bf16x2(c[2], true),
-                        fp8x2_to_bf16x2(c[3], false), fp8x2_to_bf16x2(c[3], true)};
-      *reinterpret_cast<u32x4*>(buf + vst0) = lo;
-      *reinterpret_cast<u32x4*>(buf + vst1) = hi;
-    }
-  };
+  // ... and its chunks of a bf16 V tile
+  uint32_t vdma[V16::CPT];
+#pragma unroll
+  for (int n = 0; n < V16::CPT; ++n) {
+    const int P = (wid * V16::CPT + n) * 64 + lane;
+    const int row = P / V16::CPR, ch = (P % V16::CPR) ^ swz<D>(row);
+    vdma[n] = (uint32_t)row * (2 * rs) + ch * 16;
+  }
   // LDS read offsets (tile-relative):
   //  K for step ks: row ql, chunks 4 ks + 2 hl and 4 ks + 2 hl + 1
   uint32_t koffs[C::NS][2];
@@ -775,25 +774,21 @@ void fwd8_kernel(FwdParams p) {
 
   if (t0 < t1) {
     dma_k(lk0, (uint32_t)(t0 * BN) * rs);
-    u32x4 vc = has_chunk ? bload16(vr, (uint32_t)(t0 * BN) * rs + vld) : u32x4{};
-    wait_vm_all();
-    store_v(lv0, vc);
+    dma_tile<E_BF16, D, 1>(lv0, vrs, (uint32_t)(t0 * BN) * 2 * rs, wid, vdma);
   }
-  lds_barrier();
-  // nothing is in flight here on any path; saying so keeps the compiler's
-  // wait insertion from carrying the Q code loads into the tile loop as
-  // pending, where it would wait for each tile's prefetch before the
-  // tile's second score MFMA
+  // on every path (with no tile too), so that no load, the Q codes included,
+  // is in flight when the tile loop starts: otherwise the compiler's wait
+  // insertion carries the Q code loads into the loop as pending and waits for
+  // each tile's prefetch before the tile's second score MFMA
   wait_vm_all();
+  lds_barrier();
 
   auto tile = [&](int t, const uint8_t* kb_, const uint8_t* vb_, uint8_t* knext,
                   uint8_t* vnext) __attribute__((always_inline)) {
-    const bool more = t + 1 < t1;
-    u32x4 vc = {};
-    if (more) {
+    if (t + 1 < t1) {
       const uint32_t base = (uint32_t)((t + 1) * BN) * rs;
       dma_k(knext, base);
-      if (has_chunk) vc = bload16(vr, base + vld);
+      dma_tile<E_BF16, D, 1>(vnext, vrs, 2 * base, wid, vdma);
     }
     const int c0 = t * BN;
     if (t >= tv0 && t < tv1) {
@@ -856,9 +851,8 @@ void fwd8_kernel(FwdParams p) {
       }
       sched_lds_ahead<2 * C::NOB, 2, 2>();
     }
-    wait_vm_all();            // K(t+1) DMA and the V(t+1) codes have landed
-    if (more) store_v(vnext, vc);
-    lds_barrier();            // ... for everyone, and V(t+1) is written
+    wait_vm_all();  // the K and V DMA of tile t+1 have landed (this wave's part)
+    lds_barrier();  // ... and everyone's
   };
 
   int t = t0;

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <cstdint>
 #include <string>
 
@@ -146,6 +147,43 @@ int varlen_attention_fwd(const void* q, const void* k, const void* v,
   return finish_and_launch(p, max_seqlen_q, elem, head_dim, hip_stream);
 }
 
+// Stream-ordered scratch for the FP8 forward's bf16 copy of V: a memory pool
+// per device, owned by the library, that keeps what it has reserved (release
+// threshold at its maximum), so after the first call of a given size the
+// allocation is bookkeeping on the stream, not a device allocation.  Each
+// block lives from its allocation to its free on the caller's stream, so
+// concurrent calls on different streams get different blocks.
+namespace {
+constexpr int kMaxPoolDevices = 64;
+std::mutex g_pool_mutex;
+hipMemPool_t g_pools[kMaxPoolDevices] = {};
+
+hipError_t scratch_pool(hipMemPool_t* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxPoolDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_pool_mutex);
+  if (g_pools[dev] == nullptr) {
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if ((e = hipMemPoolCreate(&pool, &props)) != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;
+    if ((e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
+      hipMemPoolDestroy(pool);
+      return e;
+    }
+    g_pools[dev] = pool;
+  }
+  *out = g_pools[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 static int dense_common(const void* q, const void* k, const void* v, int64_t batch,
                         int64_t num_heads, int64_t num_kv_heads, int64_t seqlen_q,
                         int64_t kv_capacity, int64_t head_dim, int causal, int64_t window_size,
@@ -192,7 +230,27 @@ static int dense_common(const void* q, const void* k, const void* v, int64_t bat
   p.window = (int32_t)window_size;
   p.score_mul = (float)score_mul;
   p.out_mul = (float)out_mul;
-  return finish_and_launch(p, seqlen_q, elem, head_dim, hip_stream);
+  if (elem != vlgqa::E_E4M3 || n == 0) return finish_and_launch(p, seqlen_q, elem, head_dim, hip_stream);
+
+  // E4M3: the kernel takes V as its exact bf16 copy (same element strides),
+  // made here on the caller's stream into a stream-ordered scratch block
+  const hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int64_t codes = batch * num_kv_heads * kv_capacity * head_dim;
+  hipMemPool_t pool = nullptr;
+  void* wide = nullptr;
+  hipError_t e = scratch_pool(&pool);
+  if (e == hipSuccess) e = hipMallocFromPoolAsync(&wide, (size_t)codes * 2, pool, stream);
+  if (e != hipSuccess) return fail(VLGQA_EHIP, "scratch", hipGetErrorString(e));
+  e = vlgqa::launch_widen_e4m3(v, wide, codes, stream);
+  if (e == hipSuccess) {
+    p.v = wide;
+    rc = finish_and_launch(p, seqlen_q, elem, head_dim, hip_stream);
+  } else {
+    rc = fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
+  }
+  e = hipFreeAsync(wide, stream);
+  if (e != hipSuccess && rc == VLGQA_OK) rc = fail(VLGQA_EHIP, "scratch", hipGetErrorString(e));
+  return rc;
 }
 
 int flash_attention_fwd(const void* q, const void* k, const void* v, int64_t batch,

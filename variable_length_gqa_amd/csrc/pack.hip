@@ -1,6 +1,7 @@
 // Packing of padded batches into the varlen layout (gfx950): the exclusive
 // prefix sum of the sequence lengths (cu_seqlens) and the row copies padded
-// [B, S, row] <-> packed [total, row].  boostr 0.2.0 varlen_attention.rs:
+// [B, S, row] <-> packed [total, row]; and the E4M3 -> bf16 widening copy the
+// FP8 paths use.  boostr 0.2.0 varlen_attention.rs:
 // sequences of different lengths are packed into one buffer instead of being
 // padded; cu_seqlens[0] = 0, cu_seqlens[i] = sum of lengths 0..i-1.  Rows are
 // opaque bytes (a multiple of 16), moved as 16-byte vectors.
@@ -117,7 +118,37 @@ unsigned grid_for_rows(int64_t rows) {
   return (unsigned)(blocks < 2048 ? blocks : 2048);
 }
 
+// E4M3 codes -> bf16 (exact: every E4M3 value is a bf16 value), 16 codes per
+// thread (n16 = codes / 16)
+__global__ __launch_bounds__(256) void widen_e4m3_kernel(const uint8_t* __restrict__ src,
+                                                         uint16_t* __restrict__ dst, int64_t n16) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const u32x4 c = *reinterpret_cast<const u32x4*>(src + i * 16);
+  u32x4 w[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[k], 1.0f, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[k], 1.0f, true);
+    w[k >> 1][2 * (k & 1)] = __builtin_bit_cast(uint32_t, lo);
+    w[k >> 1][2 * (k & 1) + 1] = __builtin_bit_cast(uint32_t, hi);
+  }
+  *reinterpret_cast<u32x4*>(dst + i * 16) = w[0];
+  *reinterpret_cast<u32x4*>(dst + i * 16 + 8) = w[1];
+}
+
 }  // namespace
+
+hipError_t launch_widen_e4m3(const void* codes, void* bf16, int64_t n, hipStream_t stream) {
+  if (n % 16 != 0) return hipErrorInvalidValue;
+  const int64_t n16 = n / 16;
+  if (n16 > 0)
+    hipLaunchKernelGGL(widen_e4m3_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0,
+                       stream, reinterpret_cast<const uint8_t*>(codes),
+                       reinterpret_cast<uint16_t*>(bf16), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_cu_seqlens(const int32_t* lengths, int64_t batch, int32_t* cu,
                              hipStream_t stream) {
