@@ -130,6 +130,24 @@ def test_varlen_rows_beyond_max_seqlen_are_nan(dtype):
     assert_close("LSE", l.double().numpy()[keep], L[keep], tl)
 
 
+def test_two_heads_per_workgroup_rows_beyond_max_seqlen_are_nan():
+    """max_seqlen_q >= 4096 with an even group: the 16-bit kernel takes two
+    heads of 64 rows per workgroup.  Every row within the launch's reach (65
+    tiles of 64 rows = 4160) matches the oracle in both heads of each pair, and
+    the rows of the 4200-token sequence past it are NaN in every head."""
+    x = W.make_varlen([4200, 10], num_heads=4, num_kv_heads=2, head_dim=128,
+                      dtype=torch.bfloat16, causal=True, seed=161)
+    out = torch.zeros((4210, 4, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros((4210, 4), dtype=torch.float32, device=DEV)
+    o, l = run_varlen(x, out=out, lse=lse, max_q=4100)
+    assert torch.isnan(o[4160:4200].float()).all() and torch.isnan(l[4160:4200]).all()
+    O, L = oracle.varlen_attention_fwd(x.q, x.k, x.v, x.cu_q, x.cu_k, 4, 2, True)
+    keep = np.r_[0:4160, 4200:4210]
+    to, tl = TOL[torch.bfloat16]
+    assert_close("O", to_f64(o)[keep], O[keep], to, torch.bfloat16)
+    assert_close("LSE", l.double().numpy()[keep], L[keep], tl)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=str)
 def test_causal_first_row_is_v0_bit_exact(dtype):
     x = W.make_varlen([300, 1, 129], num_heads=8, num_kv_heads=2, head_dim=128, dtype=dtype,
