@@ -1,7 +1,8 @@
 """The entry points under HIP graph capture: the library enqueues on the
-caller's stream, never synchronises and allocates nothing, so a forward +
-backward step (and a decode step) captured once replays with the results of
-the eager calls.  Each graph is replayed several times with eager work and
+caller's stream and never synchronises, so a forward + backward step (and a
+decode step, and an FP8 forward, whose scratch block for the bf16 copy of V is
+taken and given back in stream order) captured once replays with the results
+of the eager calls.  Each graph is replayed several times with eager work and
 synchronisation in between, and every replay is compared bit for bit."""
 
 import pytest
@@ -71,6 +72,30 @@ def test_decode_step_replays_in_a_graph():
                                   workspace=ws)
 
     step()
+    torch.cuda.synchronize()
+    eager = [out.clone(), lse.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = torch.randn(1 << 20, device=DEV)
+    _replay_and_compare(g, [out, lse], eager, lambda: other.mul_(1.0001))
+
+
+def test_fp8_forward_replays_in_a_graph():
+    d = W.make_dense_fp8(2, 8, 2, 700, 128, causal=True, seed=803).to(DEV)
+    s = d.scales
+    out = torch.empty(d.q.shape, dtype=torch.uint8, device=DEV)
+    lse = torch.empty(d.q.shape[:3], dtype=torch.float32, device=DEV)
+
+    def step():
+        vg.flash_attention_fwd_fp8(d.q, d.k, d.v, 8, 2, 128, True, s["q_scale"], s["k_scale"],
+                                   s["v_scale"], 0.05, out=out, lse=lse)
+
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step()
+    torch.cuda.current_stream().wait_stream(st)
     torch.cuda.synchronize()
     eager = [out.clone(), lse.clone()]
     g = torch.cuda.CUDAGraph()

@@ -89,3 +89,42 @@ def test_repeated_forward_launches_on_one_stream_are_identical():
         else:
             o, l = run()
         assert torch.equal(o, o0) and torch.equal(l, l0), i
+
+
+def _fp8_problem(seed, batch, seqlen):
+    d = W.make_dense_fp8(batch, 8, 2, seqlen, 128, causal=True, seed=seed).to(DEV)
+    s = d.scales
+    out = torch.empty(d.q.shape, dtype=torch.uint8, device=DEV)
+    lse = torch.empty(d.q.shape[:3], dtype=torch.float32, device=DEV)
+    return d, s, out, lse
+
+
+def _fp8_step(d, s, out, lse):
+    vg.flash_attention_fwd_fp8(d.q, d.k, d.v, 8, 2, 128, True, s["q_scale"], s["k_scale"],
+                               s["v_scale"], 0.05, out=out, lse=lse)
+
+
+def test_fp8_forward_on_two_streams_matches_sequential():
+    """The FP8 forward widens V into a scratch block taken in stream order from
+    the library's pool: calls on two streams at once, of different sizes, each
+    repeated, get blocks of their own and the results of sequential calls."""
+    pa = _fp8_problem(920, 2, 1500)
+    pb = _fp8_problem(930, 3, 700)
+    _fp8_step(*pa)
+    _fp8_step(*pb)
+    torch.cuda.synchronize()
+    want = [(p[2].clone(), p[3].clone()) for p in (pa, pb)]
+    for p in (pa, pb):
+        p[2].zero_()
+        p[3].fill_(float("nan"))
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    for _ in range(4):
+        with torch.cuda.stream(sa):
+            _fp8_step(*pa)
+        with torch.cuda.stream(sb):
+            _fp8_step(*pb)
+    torch.cuda.synchronize()
+    for p, (o, l) in zip((pa, pb), want):
+        assert torch.equal(p[2], o) and torch.equal(p[3], l)
