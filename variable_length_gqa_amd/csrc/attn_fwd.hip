@@ -35,6 +35,7 @@
 
 #include "fwd_params.h"
 #include "kernel_common.h"
+#include "ticket.h"
 
 namespace vlgqa {
 
@@ -1063,20 +1064,16 @@ bool plan_fwd(FwdParams& p, int elem, int head_dim) {
 #endif
 constexpr int kTicketSlots = 64;    // streams per device with run-time hand-out
 constexpr int kTicketDevices = 64;
-constexpr int kTailDivisor = 5;     // a fifth of every XCD's slots is claimed at run time
 constexpr int kNkb = VLGQA_NKB;  // 32-key blocks per tile of the bf16/f16 kernel
 constexpr int kWpe = VLGQA_WPE;  // its waves per SIMD (D = 128)
 constexpr int kWpe64 = 4;        // at D = 64 (about 100 VGPRs, 16 KB of LDS a workgroup)
 
-// Claim counters of the run-time hand-out: one per (device, stream) the
-// forward has launched on, library-owned, zero when the code object loads.
-// Each launch claims exactly n_claim times; the host keeps the running count
-// per stream, and launches on one stream run one after the other, so a
-// launch's claims are the counter's next n_claim values (no reset needed).
-static __device__ unsigned fwd_ticket[kTicketSlots * 32];  // 128 bytes apart
+// Claim counters of the run-time hand-out, 128 bytes apart: one per
+// (device, stream) the forward has launched on.
+static __device__ unsigned run_ticket[kTicketSlots * 32];
 
 namespace {
-std::mutex g_ticket_mutex;  // held from a launch's claim base to its enqueue
+std::mutex g_ticket_mutex;
 unsigned* g_ticket_base_ptr[kTicketDevices] = {};
 struct TicketSlot {
   int index;
@@ -1084,54 +1081,56 @@ struct TicketSlot {
 };
 std::map<std::pair<int, hipStream_t>, TicketSlot> g_ticket_slots;
 int g_ticket_used[kTicketDevices] = {};
+}  // namespace
 
-// The (device, stream) slot, or null when the launch must use the static
-// order: a stream being captured into a graph (it may be replayed on another
-// stream), the per-thread default stream (one handle, many streams), more than
-// kTicketSlots streams on a device.  Caller holds g_ticket_mutex.
-TicketSlot* ticket_slot(hipStream_t stream, int* dev_out) {
-  if (stream == hipStreamPerThread) return nullptr;
+TicketLease ticket_lease(hipStream_t stream) {
+  TicketLease l;
+  l.lock = std::unique_lock<std::mutex>(g_ticket_mutex);
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
-    return nullptr;
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kTicketDevices) return nullptr;
+  if (stream == hipStreamPerThread ||
+      hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone ||
+      hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kTicketDevices) {
+    l.lock.unlock();
+    return l;
+  }
   if (!g_ticket_base_ptr[dev]) {
     void* a = nullptr;
-    if (hipGetSymbolAddress(&a, HIP_SYMBOL(fwd_ticket)) != hipSuccess) return nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(run_ticket)) != hipSuccess) {
+      l.lock.unlock();
+      return l;
+    }
     g_ticket_base_ptr[dev] = static_cast<unsigned*>(a);
   }
   auto key = std::make_pair(dev, stream);
   auto it = g_ticket_slots.find(key);
   if (it == g_ticket_slots.end()) {
-    if (g_ticket_used[dev] >= kTicketSlots) return nullptr;
+    if (g_ticket_used[dev] >= kTicketSlots) {
+      l.lock.unlock();
+      return l;
+    }
     it = g_ticket_slots.emplace(key, TicketSlot{g_ticket_used[dev]++, 0u}).first;
   }
-  *dev_out = dev;
-  return &it->second;
+  l.counter = g_ticket_base_ptr[dev] + 32 * it->second.index;
+  l.next = &it->second.next;
+  return l;
 }
-}  // namespace
 
 hipError_t launch_fwd(const FwdParams& p0, int elem, int head_dim, hipStream_t stream) {
   FwdParams p = p0;
-  std::unique_lock<std::mutex> lock(g_ticket_mutex, std::defer_lock);
-  TicketSlot* slot = nullptr;
+  TicketLease lease;
   {
     const int G2 = p.group / p.heads_per_wg;
     const int64_t slots = ((int64_t)p.n_groups + 7) / 8 * G2;  // per XCD
-    const int64_t tail = slots / kTailDivisor;
-    if (tail >= 2 && slots * 8 < INT32_MAX / 2) {
-      lock.lock();
-      int dev = 0;
-      slot = ticket_slot(stream, &dev);
-      if (slot) {
-        p.ticket = g_ticket_base_ptr[dev] + 32 * slot->index;
-        p.ticket_base = slot->next;
+    const int64_t tail = tail_slots(slots);
+    if (tail > 0) {
+      lease = ticket_lease(stream);
+      if (lease.counter) {
+        p.ticket = lease.counter;
+        p.ticket_base = lease.base();
         p.n_static = (int32_t)(slots - tail);
         p.n_tail = (int32_t)(8 * tail);
-        p.n_claim = (int32_t)(8 * (tail + tail / 10 + 1));  // ~10% spares
-      } else {
-        lock.unlock();
+        p.n_claim = (int32_t)claim_blocks(tail);
       }
     }
   }
@@ -1161,7 +1160,7 @@ hipError_t launch_fwd(const FwdParams& p0, int elem, int head_dim, hipStream_t s
 #undef VLGQA_LAUNCH
   const hipError_t e = hipGetLastError();
   // the counter moves only for a launch that was enqueued
-  if (slot && e == hipSuccess) slot->next += (unsigned)p.n_claim;
+  if (p.ticket && e == hipSuccess) lease.advance((unsigned)p.n_claim);
   return e;
 }
 
