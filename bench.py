@@ -45,7 +45,9 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {
     "forward": ["variable_length_gqa_amd/csrc/attn_fwd.hip",
                 "variable_length_gqa_amd/csrc/fwd_params.h",
-                "variable_length_gqa_amd/csrc/kernel_common.h"],
+                "variable_length_gqa_amd/csrc/kernel_common.h",
+                "variable_length_gqa_amd/csrc/ticket.h",
+                "variable_length_gqa_amd/csrc/pack.hip"],
     "backward": ["variable_length_gqa_amd/csrc/attn_bwd.hip",
                  "variable_length_gqa_amd/csrc/bwd_params.h",
                  "variable_length_gqa_amd/csrc/kernel_common.h"],
