@@ -345,14 +345,22 @@ def cpu_baseline_bwd(name, x, n_heads, unit_scale):
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    """The host CPU's model name from /proc/cpuinfo, with its family / model /
+    stepping numbers (a virtualised host may report only a generic name), or
+    the platform's processor string."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.lower().startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block
+                k, _, v = line.partition(":")
+                info.setdefault(k.strip().lower(), v.strip())
     except OSError:
         pass
+    if "model name" in info:
+        ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+        return info["model name"] + (f" ({', '.join(ids)})" if ids else "")
     import platform
 
     return platform.processor() or "unknown"
