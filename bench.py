@@ -5,8 +5,9 @@
                     [--cpu-heads N]
 
 One step = one call of the forward entry point over the whole workload (the
-complete hot path: a single fused kernel launch), inputs already resident in
-HBM, outputs preallocated.  The default workload is the long-context packed
+complete hot path: a single fused kernel launch; the FP8 forward adds the
+launch that widens V to bf16), inputs already resident in HBM, outputs
+preallocated.  The default workload is the long-context packed
 batch: lengths [8192, 4096, 2048, 2048] (16384 tokens), H=64, Hkv=8, D=128,
 bf16, causal.
 
