@@ -390,11 +390,17 @@ void bwd_kv_kernel(BwdParams p) {
   tr_read_offsets<D>(troff, lane);
   const int64_t plane = ws_plane(p);
 
-  // DMA of stage s into buffer u: the tiles of (head, tile) and its lse2/delta
-  auto issue = [&](int s, auto U) __attribute__((always_inline)) {
-    const int hh = s % gsplit, t = tb - 1 - s / gsplit;
-    const int h = hbase + hh;
-    const int64_t qrow0 = (int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs + (int64_t)h * p.q_hs;
+  // DMA of the next stage into buffer U: the tiles of its (head, query tile)
+  // and their lse2 / delta.  The stage's query tile and the row offsets of its
+  // head in Q / dO and in the workspace are carried from stage to stage (no
+  // division by the head count in the loop).
+  const int64_t qhead0 = (int64_t)b * p.q_bs + (int64_t)sb.q_start * p.q_rs + (int64_t)hbase * p.q_hs;
+  const int64_t whead0 = ws_index(p, p.cu_q ? 0 : b, p.cu_q ? (int64_t)sb.q_start : 0, hbase);
+  int iss_h = 0, iss_t = tb - 1;
+  int64_t iss_q = qhead0, iss_w = whead0;
+  auto issue = [&](auto U) __attribute__((always_inline)) {
+    const int t = iss_t;
+    const int64_t qrow0 = iss_q;
     const uint32_t bytes = sat_bytes((int64_t)sb.Lq * p.q_rs * 2);
     const uint32_t base = (uint32_t)(t * 32) * (uint32_t)(p.q_rs * 2);
     const uint8_t* buf = stage_buf(U);
@@ -421,24 +427,36 @@ void bwd_kv_kernel(BwdParams p) {
     if (wid < 2 && lane < 8) {
       // wave 0: lse2 of rows 32 t .. +32 (4 per lane), wave 1: delta; rows past
       // the sequence arrive as zeros
-      const int64_t wi = ws_index(p, p.cu_q ? 0 : b, p.cu_q ? (int64_t)sb.q_start : 0, h);
-      const float* src = p.delta + wi + (wid == 1 ? plane : 0);
+      const float* src = p.delta + iss_w + (wid == 1 ? plane : 0);
       dma16(buf + OFF_W + wid * 128, (uint32_t)(t * 32 * 4 + lane * 16),
             make_rsrc(src, sat_bytes((int64_t)sb.Lq * 4)));
+    }
+    if (++iss_h == gsplit) {
+      iss_h = 0;
+      --iss_t;
+      iss_q = qhead0;
+      iss_w = whead0;
+    } else {
+      iss_q += p.q_hs;
+      iss_w += p.d_rows;
     }
   };
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  if (nst > 0) issue(0, S0{});
+  if (nst > 0) issue(S0{});
   wait_vm_all();
   lds_barrier();
 
   // stage s sits in buffer s % 2
+  int cur_h = 0, cur_t = tb - 1;  // the stage computed next
   auto stage = [&](int s, auto U) __attribute__((always_inline)) {
-    if (s + 1 < nst) issue(s + 1, std::integral_constant<int, 1 - decltype(U)::value>{});
-    const int t = tb - 1 - s / gsplit;
-    const int q0 = t * 32;
+    if (s + 1 < nst) issue(std::integral_constant<int, 1 - decltype(U)::value>{});
+    const int q0 = cur_t * 32;
+    if (++cur_h == gsplit) {
+      cur_h = 0;
+      --cur_t;
+    }
     if (wave_keys && q0 < wqb && q0 + 32 > wqa) {
       const uint8_t* sbuf = stage_buf(U);
       const uint8_t* st_ = sbuf + OFF_S;    // A operand of S (Q rows)

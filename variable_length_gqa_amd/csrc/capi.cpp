@@ -174,7 +174,7 @@ hipError_t scratch_pool(hipMemPool_t* out) {
     if ((e = hipMemPoolCreate(&pool, &props)) != hipSuccess) return e;
     uint64_t keep = UINT64_MAX;
     if ((e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
-      hipMemPoolDestroy(pool);
+      (void)hipMemPoolDestroy(pool);  // the attribute error is the one reported
       return e;
     }
     g_pools[dev] = pool;
