@@ -39,6 +39,21 @@ sys.path.insert(0, ROOT)
 
 METRIC = "varlen causal GQA attn fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 METRIC_BWD = "varlen causal GQA attn bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+HEADLINE_WORKLOAD = "varlen_bf16_long"
+
+
+def metric_name(cfg: dict, bwd: bool, dtype: str) -> str:
+    """The headline metric for the long-context workload; for the others the
+    same form, naming their layout, mask, head grouping and peak."""
+    if cfg.get("workload") == HEADLINE_WORKLOAD:
+        return METRIC_BWD if bwd else METRIC
+    layout = "varlen" if cfg.get("layout") == "packed varlen" else "dense"
+    mask = "windowed " if cfg.get("window") else ("causal " if cfg.get("causal") else "")
+    group = "GQA" if cfg.get("kv_heads", 0) < cfg.get("heads", 0) else "MHA"
+    return (f"{layout} {mask}{group} attn {'bwd' if bwd else 'fwd'} TFLOP/s on 1 MI355X; "
+            f"% of {dtype} MFMA peak")
+
+
 METRIC_PACK = "padded <-> packed varlen copy GB/s on 1 MI355X; % of HBM peak"
 METRIC_DECODE = "KV-cache decode attn fwd GB/s on 1 MI355X; % of HBM peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "f32": 157.3}
@@ -467,7 +482,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="varlen_bf16_long")
+    ap.add_argument("--workload", default=HEADLINE_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-ms", type=float, default=150.0,
                     help="untimed steps for about this long before the warm-up steps, so "
@@ -520,7 +535,7 @@ def main():
     traffic = measured_traffic(args.workload, args.which)
 
     res = {
-        "metric": METRIC_BWD if bwd else METRIC, "value": round(tflops, 2), "unit": "TFLOP/s",
+        "metric": metric_name(cfg, bwd, dt), "value": round(tflops, 2), "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
