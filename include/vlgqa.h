@@ -47,7 +47,9 @@
  *     the dense layouts) through 32-bit byte offsets, so (length + 128) x
  *     (row stride in bytes) must stay below 4 GiB for q and for k/v (packed:
  *     the row stride is heads x head_dim elements, e.g. 262,016 tokens at 64
- *     bf16 heads of 128); longer sequences return EINVAL.
+ *     bf16 heads of 128); longer sequences return EINVAL.  The FP8 entry
+ *     points count k/v (forward: v) at 2 bytes per element: they read 16-bit
+ *     copies of the codes.
  */
 #ifndef VLGQA_H
 #define VLGQA_H

@@ -382,6 +382,10 @@ def test_sequences_past_32bit_buffer_offsets_are_rejected(lib):
     assert err(lib).startswith("kv_seq_len:"), err(lib)
     assert bwd8(lib, b=1, sq=64, sk=1 << 24) == EINVAL
     assert err(lib).startswith("seqlen_k:"), err(lib)
+    # the FP8 forward reads V as a 16-bit copy: 20M keys x 128 x 2 B pass the
+    # 1-byte code check but not the copy's
+    assert fp8(lib, b=1, sq=64, sk=20_000_000) == EINVAL
+    assert err(lib).startswith("kv_seq_len:"), err(lib)
 
 
 def test_noalloc_decode_rejects_on_the_host(lib):

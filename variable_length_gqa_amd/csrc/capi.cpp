@@ -204,7 +204,9 @@ static int dense_common(const void* q, const void* k, const void* v, int64_t bat
   if (window_size > INT32_MAX) window_size = INT32_MAX;
   if (batch == 0 || seqlen_q == 0) return VLGQA_OK;
   if ((rc = check_span(seqlen_q, head_dim * elem_bytes(elem), "seqlen_q"))) return rc;
-  if ((rc = check_span(n, head_dim * elem_bytes(elem), "kv_seq_len"))) return rc;
+  // E4M3: the kernel reads V as its 16-bit copy
+  const int64_t v_bytes = elem == vlgqa::E_E4M3 ? 2 : elem_bytes(elem);
+  if ((rc = check_span(n, head_dim * v_bytes, "kv_seq_len"))) return rc;
   if ((rc = check_ptr(q, "q"))) return rc;
   if (n > 0) {
     if ((rc = check_ptr(k, "k"))) return rc;
