@@ -22,10 +22,17 @@
  *     untouched).
  *   - Tensors are contiguous in the layouts stated per entry point; extents
  *     that a tensor's shape would carry are passed as scalars.
- *   - The library allocates nothing, frees nothing and never synchronises:
- *     kernels are enqueued on `hip_stream` (a hipStream_t; NULL = the null
- *     stream) and the call returns at once.  Buffers must stay alive until the
- *     stream work completes.
+ *   - The library never synchronises: kernels are enqueued on `hip_stream`
+ *     (a hipStream_t; NULL = the null stream) and the call returns at once.
+ *     Buffers must stay alive until the stream work completes.  It allocates
+ *     and frees nothing, except the FP8 forward's stream-ordered scratch block
+ *     (see flash_attention_fwd_fp8).
+ *   - The launch runs on the device `hip_stream` belongs to (the current
+ *     device for the null, legacy and per-thread streams), and the pointers
+ *     must be that device's memory.  While a call runs it makes that device
+ *     current and restores the caller's current device before returning, so
+ *     the library's per-device state (claim counters, the decode's static
+ *     scratch, the FP8 scratch pool) is always the launch device's.
  *   - Forward launches hand out their last items at run time (faster XCDs
  *     take more of them) from a claim counter the library owns: one 4-byte
  *     device counter per (device, stream) a forward has been launched on, zero
@@ -176,7 +183,7 @@ int flash_attention_decode(const void* q, const void* k, const void* v,
  *   Every call on one GPU shares that GPU's array: calls that may overlap on
  *   one GPU (different streams, or different host threads) race and must be
  *   ordered by the caller, e.g. on one stream.  EHIP if the array's address
- *   cannot be found on the current device.
+ *   cannot be found on the launch device (the device of hip_stream).
  */
 int flash_attention_decode_noalloc(const void* q, const void* k, const void* v,
                                    int64_t batch, int64_t num_heads, int64_t num_kv_heads,

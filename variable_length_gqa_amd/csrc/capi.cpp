@@ -58,6 +58,36 @@ int check_span(int64_t rows, int64_t row_bytes, const char* name) {
   return VLGQA_OK;
 }
 
+// Makes the device that `stream` belongs to current for the guard's lifetime
+// and restores the caller's current device afterwards.  The library's
+// per-device state (the forward's claim counters, the decode's static scratch,
+// the FP8 scratch pool) is looked up on the current device, so it must be the
+// device the launch runs on.  The null, legacy and per-thread default streams
+// belong to the current device.
+class StreamDeviceGuard {
+ public:
+  explicit StreamDeviceGuard(hipStream_t stream) {
+    int cur = -1;
+    if ((err_ = hipGetDevice(&cur)) != hipSuccess) return;
+    if (stream == nullptr || stream == hipStreamLegacy || stream == hipStreamPerThread) return;
+    hipDevice_t dev = 0;
+    if ((err_ = hipStreamGetDevice(stream, &dev)) != hipSuccess) return;
+    if ((int)dev == cur) return;
+    if ((err_ = hipSetDevice((int)dev)) != hipSuccess) return;
+    prev_ = cur;
+  }
+  ~StreamDeviceGuard() {
+    if (prev_ >= 0) (void)hipSetDevice(prev_);  // the device was current when the call began
+  }
+  StreamDeviceGuard(const StreamDeviceGuard&) = delete;
+  StreamDeviceGuard& operator=(const StreamDeviceGuard&) = delete;
+  hipError_t error() const { return err_; }
+
+ private:
+  int prev_ = -1;
+  hipError_t err_ = hipSuccess;
+};
+
 int elem_bytes(int elem) { return elem == vlgqa::E_F32 ? 4 : elem == vlgqa::E_E4M3 ? 1 : 2; }
 
 int elem_of_dtype(int dtype, int* elem) {
@@ -69,15 +99,28 @@ int elem_of_dtype(int dtype, int* elem) {
   }
 }
 
-int finish_and_launch(vlgqa::FwdParams& p, int64_t max_seqlen_q, int elem, int64_t head_dim,
-                      void* hip_stream) {
+// host part of a forward launch: the grid plan (no HIP call)
+int plan_launch(vlgqa::FwdParams& p, int64_t max_seqlen_q, int elem, int64_t head_dim) {
   if (max_seqlen_q > INT32_MAX) return fail(VLGQA_EINVAL, "max_seqlen_q", "too large");
   p.max_seqlen_q = (int32_t)max_seqlen_q;
   if (!vlgqa::plan_fwd(p, elem, (int)head_dim))
     return fail(VLGQA_EINVAL, "max_seqlen_q", "problem too large for one launch");
-  hipError_t e = vlgqa::launch_fwd(p, elem, (int)head_dim, reinterpret_cast<hipStream_t>(hip_stream));
+  return VLGQA_OK;
+}
+
+int launch_planned(const vlgqa::FwdParams& p, int elem, int64_t head_dim, hipStream_t stream) {
+  const StreamDeviceGuard guard(stream);
+  if (guard.error() != hipSuccess) return fail(VLGQA_EHIP, "hip_stream", hipGetErrorString(guard.error()));
+  hipError_t e = vlgqa::launch_fwd(p, elem, (int)head_dim, stream);
   if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
   return VLGQA_OK;
+}
+
+int finish_and_launch(vlgqa::FwdParams& p, int64_t max_seqlen_q, int elem, int64_t head_dim,
+                      void* hip_stream) {
+  int rc;
+  if ((rc = plan_launch(p, max_seqlen_q, elem, head_dim))) return rc;
+  return launch_planned(p, elem, head_dim, reinterpret_cast<hipStream_t>(hip_stream));
 }
 
 }  // namespace
@@ -236,7 +279,10 @@ static int dense_common(const void* q, const void* k, const void* v, int64_t bat
 
   // E4M3: the kernel takes V as its exact bf16 copy (same element strides),
   // made here on the caller's stream into a stream-ordered scratch block
+  if ((rc = plan_launch(p, seqlen_q, elem, head_dim))) return rc;
   const hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const StreamDeviceGuard guard(stream);  // the pool is the stream's device's
+  if (guard.error() != hipSuccess) return fail(VLGQA_EHIP, "hip_stream", hipGetErrorString(guard.error()));
   const int64_t codes = batch * num_kv_heads * kv_capacity * head_dim;
   hipMemPool_t pool = nullptr;
   void* wide = nullptr;
@@ -246,7 +292,7 @@ static int dense_common(const void* q, const void* k, const void* v, int64_t bat
   e = vlgqa::launch_widen_e4m3(v, wide, codes, stream);
   if (e == hipSuccess) {
     p.v = wide;
-    rc = finish_and_launch(p, seqlen_q, elem, head_dim, hip_stream);
+    rc = launch_planned(p, elem, head_dim, stream);
   } else {
     rc = fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
   }
@@ -344,11 +390,13 @@ static int decode_common(const void* q, const void* k, const void* v, int64_t ba
   }
   if ((rc = check_ptr(out, "out"))) return rc;
   if ((rc = check_ptr(lse, "lse"))) return rc;
+  if (!static_scratch && (rc = check_ptr(workspace, "workspace"))) return rc;
+  const hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const StreamDeviceGuard guard(stream);  // the static scratch is the stream's device's
+  if (guard.error() != hipSuccess) return fail(VLGQA_EHIP, "hip_stream", hipGetErrorString(guard.error()));
   if (static_scratch) {
     hipError_t se = vlgqa::decode_scratch(&workspace);
     if (se != hipSuccess) return fail(VLGQA_EHIP, "scratch", hipGetErrorString(se));
-  } else if ((rc = check_ptr(workspace, "workspace"))) {
-    return rc;
   }
 
   vlgqa::DecParams p{};
@@ -367,8 +415,7 @@ static int decode_common(const void* q, const void* k, const void* v, int64_t ba
   p.n_parts = (int32_t)parts;
   p.score_mul = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   p.out_mul = 1.0f;
-  hipError_t e = vlgqa::launch_decode(p, elem, (int)head_dim,
-                                      reinterpret_cast<hipStream_t>(hip_stream));
+  hipError_t e = vlgqa::launch_decode(p, elem, (int)head_dim, stream);
   if (e != hipSuccess) return fail(VLGQA_EHIP, "launch", hipGetErrorString(e));
   return VLGQA_OK;
 }
