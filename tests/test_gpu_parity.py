@@ -148,6 +148,28 @@ def test_two_heads_per_workgroup_rows_beyond_max_seqlen_are_nan():
     assert_close("LSE", l.double().numpy()[keep], L[keep], tl)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=str)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_two_heads_per_workgroup(dtype, D, causal):
+    """max_seqlen_q >= 4096 with an even group: the 16-bit kernel's two-head
+    form (64 rows of two query heads per workgroup).  Ragged lengths with an
+    empty sequence, one of exactly 4096 rows and unequal q / k lengths (rows
+    without keys under the causal bound), every element against the oracle."""
+    x = W.make_varlen([4133, 0, 700, 4096], [4133, 9, 1500, 4000], num_heads=4, num_kv_heads=2,
+                      head_dim=D, dtype=dtype, causal=causal, seed=162)
+    check_varlen(x)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=str)
+def test_dense_window_two_heads_per_workgroup(dtype):
+    """The dense layout with a capacity stride and a sliding window on the
+    two-head form: 4100 query rows, 4150 of 4200 key slots, window 1000."""
+    d = W.make_dense(2, 4, 2, 4100, 64, dtype=dtype, causal=True, window=1000, kv_seq_len=4150,
+                     capacity=4200, seed=163)
+    check_dense(d)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=str)
 def test_causal_first_row_is_v0_bit_exact(dtype):
     x = W.make_varlen([300, 1, 129], num_heads=8, num_kv_heads=2, head_dim=128, dtype=dtype,
