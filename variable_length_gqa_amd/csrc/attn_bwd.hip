@@ -24,11 +24,14 @@
 //                      launches of one body): one workgroup per (sequence,
 //                      kv head, 128-key tile), 4 waves x 32 keys; K of the
 //                      wave's keys stays in registers, V in LDS (E4M3: both
-//                      in registers); the loop runs over the G query heads and
-//                      the 32-row query tiles that see the keys, with Q, dO
-//                      and the tile's LSE / delta brought to LDS by DMA (double
-//                      buffered).  dV / dK accumulate in registers: no
-//                      atomics, deterministic.
+//                      in registers); the loop runs over the group's query
+//                      heads and the 32-row query tiles that see the keys,
+//                      with Q, dO and the tile's LSE / delta brought to LDS by
+//                      DMA (double buffered).  dV / dK accumulate in
+//                      registers: no atomics, deterministic.  On long loops
+//                      the group's heads are split in two halves, one
+//                      workgroup each, whose f32 partial sums
+//   bwd_reduce_kernel  adds in a fixed order before storing dk and dv.
 // Matrix-core formulation (v_mfma_f32_32x32x16_{bf16,f16}): every product has
 // the operand layouts of the forward kernel.  In dK/dV the lane owns a key:
 //   S  = Q K^T     A = Q rows (LDS), B = K^T (registers)  -> lane: key l % 32,

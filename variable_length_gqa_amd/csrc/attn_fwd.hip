@@ -9,9 +9,11 @@
 // ("tiled_single_head_attention"): per query row a running maximum, running
 // denominator and running weighted sum, rescaled when the maximum grows.
 //
-// Work decomposition: one workgroup = one (sequence, 128-row query tile, query
-// head); 4 waves x 32 query rows.  K/V tiles of 32 keys are staged through LDS
-// (double buffered, one barrier per tile) and shared by the 4 waves.
+// Work decomposition: one workgroup = 4 waves x 32 query rows of one sequence:
+// a 128-row query tile of one query head, or (16-bit kernel, long sequences,
+// an even group) a 64-row tile of two query heads of the group.  K/V tiles of
+// 32 keys are staged through LDS (double buffered, one barrier per tile) and
+// shared by the 4 waves.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_{bf16,f16}, wave64):
 //   S^T = K Q^T   A = K tile (32 keys x 16 d, from LDS), B = Q^T (registers)
@@ -354,20 +356,22 @@ __device__ __forceinline__ void poison_beyond_reach(const FwdParams& p, const Wo
 // bf16 / f16 kernel
 // ---------------------------------------------------------------------------
 //
-// One workgroup = 128 query rows of one head, 4 waves x 32 rows; two
-// workgroups share a CU, so the two waves on a SIMD belong to independent
-// workgroups and one's vector work (softmax) overlaps the other's matrix work.
-// Per tile of BN keys a wave does BN/4 MFMAs for S^T = K Q^T, the softmax of
-// its 32 x BN scores, and BN/4 MFMAs for O^T += V^T P^T.
+// One workgroup = 4 waves x 32 query rows (128 rows of one head, or 64 rows of
+// two heads); three workgroups share a CU at D = 128 (four at D = 64), so the
+// waves on a SIMD belong to independent workgroups and one's vector work
+// (softmax) overlaps another's matrix work.  Per tile of BN keys a wave does
+// BN/4 MFMAs for S^T = K Q^T, the softmax of its 32 x BN scores, and BN/4
+// MFMAs for O^T += V^T P^T.
 //
 // K and V tiles reach LDS by DMA (buffer loads that write LDS directly: no
 // staging registers, no vector instructions), double-buffered: the next tile
 // is requested at the start of a tile and awaited at its end, and one
 // workgroup barrier per tile publishes it.  That barrier orders LDS only, so
-// it does not drain other requests.  The DMA is written out as plain
-// instructions the compiler does not track; it would otherwise stall every
-// transposing V read on it, since it cannot tell the V buffers apart.
-// Ordering is by the explicit vmcnt wait before each barrier.  V is stored
+// it does not drain other requests.  The DMA is the compiler's buffer-to-LDS
+// builtin; the two buffers of each pair are separate __shared__ arrays and the
+// tile loop is unrolled by two, so the compiler relates every LDS read to the
+// DMA into its own buffer and does not hold it for the other one.  Ordering
+// is by the explicit vmcnt wait before each barrier.  V is stored
 // row-major and read as the V^T operand with the transposing
 // ds_read_b64_tr_b16.  Rows are stored unpadded with their 16-byte chunks
 // XOR-swizzled by the row index, which keeps both read patterns free of bank
@@ -389,9 +393,10 @@ struct Cfg5 {
   static_assert(CPT >= 1 && (TILE / 16) % kThreads == 0, "tile shape");
 };
 
-// Request one tile (rows c0 .. c0+63) of K or V into an LDS tile buffer: this
-// thread's chunk n goes to LDS chunk (wid*CPT + n)*64 + lane, from tile offset
-// voff[n].  The instruction writes LDS only (no register results).
+// Request one tile of K or V (BN rows from byte offset `base`) into an LDS
+// tile buffer: this thread's chunk n goes to LDS chunk (wid*CPT + n)*64 + lane,
+// from tile offset voff[n].  The instruction writes LDS only (no register
+// results).
 template <int ELEM, int D, int NKB>
 __device__ __forceinline__ void dma_tile(uint8_t* buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t base,
                                          int wid,
