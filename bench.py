@@ -502,7 +502,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward shards across GPUs by heads or by "
-              "sequences with no exchange, and this build runs and reports a single GPU.",
+              "sequences with no exchange; the benchmark runs on and reports one GPU.",
               file=sys.stderr)
         sys.exit(2)
 
