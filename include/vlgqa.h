@@ -42,7 +42,9 @@
  *     launches of several host threads on one stream).  A launch on a stream
  *     that is being captured into a graph, on hipStreamPerThread, or on a
  *     65th stream uses the static order instead; results are identical
- *     either way.
+ *     either way.  A new stream that receives a destroyed stream's handle
+ *     continues its counter: hipStreamDestroy waits for the stream's pending
+ *     work, so no earlier launch is still claiming.
  *   - Base pointers must be 16-byte aligned.
  *   - Return value: VLGQA_OK, or an error code; no exception crosses the ABI.
  *     vlgqa_last_error() then gives "argument: reason" (thread-local, valid

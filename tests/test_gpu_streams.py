@@ -128,3 +128,46 @@ def test_fp8_forward_on_two_streams_matches_sequential():
     torch.cuda.synchronize()
     for p, (o, l) in zip((pa, pb), want):
         assert torch.equal(p[2], o) and torch.equal(p[3], l)
+
+
+def test_stream_handle_reused_after_destroy_continues_the_counter():
+    """The runtime gives a destroyed stream's handle to the next stream it
+    creates, which then continues that stream's claim counter.  Forwards left
+    pending on a stream that is destroyed at once, then forwards on new
+    streams (most likely on the same handle): every result equals the
+    reference bit for bit."""
+    import ctypes
+    import os
+
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    x = W.make_varlen([2048, 1024, 700, 300, 33], num_heads=32, num_kv_heads=8, head_dim=128,
+                      dtype=torch.bfloat16, causal=True, seed=940).to(DEV)
+    L = max(x.lengths_q)
+    T = x.q.shape[0]
+
+    def launch(stream_handle, out, lse):
+        rc = vg._lib.load().varlen_attention_fwd(
+            x.q.data_ptr(), x.k.data_ptr(), x.v.data_ptr(), x.cu_q.data_ptr(), x.cu_k.data_ptr(),
+            T, x.k.shape[0], x.batch_size, 32, 8, L, L, 128, 1, vg._lib.VLGQA_BF16,
+            out.data_ptr(), lse.data_ptr(), stream_handle)
+        assert rc == vg._lib.VLGQA_OK, vg._lib.load().vlgqa_last_error()
+
+    ref_o, ref_l = torch.empty_like(x.q), torch.empty(T, 32, dtype=torch.float32, device=DEV)
+    vg.varlen_attention_fwd(x.q, x.k, x.v, x.cu_q, x.cu_k, x.batch_size, 32, 8, L, L, 128, True,
+                            out=ref_o, lse=ref_l)
+    torch.cuda.synchronize()
+    results, handles = [], []
+    for _ in range(3):
+        s = ctypes.c_void_p()
+        assert hip.hipStreamCreate(ctypes.byref(s)) == 0
+        handles.append(s.value)
+        for _ in range(4):
+            o = torch.full_like(x.q, float("nan"))
+            l = torch.full((T, 32), float("nan"), device=DEV)
+            torch.cuda.synchronize()  # the fills are on torch's stream
+            launch(s.value, o, l)
+            results.append((o, l))
+        assert hip.hipStreamDestroy(s) == 0  # with the launches still pending
+    torch.cuda.synchronize()
+    for i, (o, l) in enumerate(results):
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), (i, handles)
